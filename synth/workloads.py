@@ -1,0 +1,302 @@
+"""Seeded synthetic batches for one packed, ragged attention step over a
+paged KV cache.
+
+What a batch holds (all integer metadata is int32, all tensors are bf16 bit
+patterns stored as uint16):
+
+* ``cu_seqlens_q[S+1]``: cumulative query-row counts; sequence ``s`` owns
+  packed rows ``cu[s] .. cu[s+1]-1`` (the ragged layout of "Continuous
+  Batching 深入实现", section "Ragged Batch + cu_seqlens").
+* ``seq_lens[S]``: keys visible to the sequence's last row after this step's
+  rows are appended (cached prefix + this step's rows).
+* ``block_tables[S, MB]``: physical block id of each logical 16-token block
+  ("连续批处理与 PagedAttention 原理", section "block table 与地址映射");
+  entries past a sequence's last block are -1.
+* ``q[T, Hq, D]``, ``k_new / v_new[T, Hkv, D]``: this step's rows.
+* ``k_pool / v_pool[NB, Hkv, 16*D]``: the pool's contents before the step,
+  one 4 KiB tile per (block, kv head).  Every element of a referenced tile is
+  an independent N(0,1) draw; the generator does not know or care how the
+  2048 elements of a tile are ordered (token-major, dimension-major...).
+  Tiles of blocks no table references are filled with a quiet-NaN pattern
+  by default, so a reader that strays into them shows up at once.
+
+Values are N(0,1) draws rounded to bf16 (round to nearest even): uniform
+16-bit integers from ``numpy.random.Generator(PCG64(seed))`` index a table
+of the 65536 N(0,1) quantiles at (u + 0.5) / 65536, so every consumer sees
+the same bits.  Block placement is a seeded random permutation of the pool's
+block ids.  This module holds no attention arithmetic.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+NUM_Q_HEADS = 32
+NUM_KV_HEADS = 8
+QNAN_BF16 = np.uint16(0x7FC0)
+
+# seed of config i (1-based) is 149000 + i
+CONFIG_SEEDS = {i: 149000 + i for i in range(1, 6)}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return
+    the 16-bit patterns.  Inputs here are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+_NORMAL_TABLE = None
+
+
+def _normal_table() -> np.ndarray:
+    """bf16 bits of the N(0,1) quantiles at (u + 0.5) / 65536, u = 0..65535:
+    indexing it with uniform 16-bit integers samples bf16(Z), Z ~ N(0,1),
+    truncated at about 4.3 sigma."""
+    global _NORMAL_TABLE
+    if _NORMAL_TABLE is None:
+        from scipy.special import ndtri
+        z = ndtri((np.arange(65536, dtype=np.float64) + 0.5) / 65536.0)
+        _NORMAL_TABLE = f32_to_bf16_bits(z.astype(np.float32))
+    return _NORMAL_TABLE
+
+
+def bf16_normal(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0,1) draws as bf16 bits: uniform 16-bit integers from ``rng`` mapped
+    through the quantile table, in chunks so very large pools stay cheap."""
+    tab = _normal_table()
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = tab[rng.integers(0, 65536, size=e - s, dtype=np.uint16)]
+    return out.reshape(shape)
+
+
+@dataclasses.dataclass
+class Batch:
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    cu_seqlens_q: np.ndarray
+    seq_lens: np.ndarray
+    block_tables: np.ndarray
+    num_blocks: int
+    q: np.ndarray
+    k_new: np.ndarray
+    v_new: np.ndarray
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    scale: np.float32
+    shared_groups: List[Tuple[Tuple[int, ...], int]] = dataclasses.field(default_factory=list)
+    seed: int = 0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_q).astype(np.int64)
+
+    @property
+    def cached_lens(self) -> np.ndarray:
+        return self.seq_lens.astype(np.int64) - self.q_lens
+
+    @property
+    def bt_stride(self) -> int:
+        return int(self.block_tables.shape[1])
+
+
+def _blocks_needed(n_tokens: int) -> int:
+    return (n_tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
+
+
+def make_batch(
+    name: str,
+    seqs: Sequence[Tuple[int, int]],
+    *,
+    seed: int,
+    num_q_heads: int = NUM_Q_HEADS,
+    num_kv_heads: int = NUM_KV_HEADS,
+    head_dim: int = HEAD_DIM,
+    num_blocks: Optional[int] = None,
+    pool_factor: float = 1.25,
+    shared_groups: Sequence[Tuple[Sequence[int], int]] = (),
+    unused_fill: str = "nan",
+    pool: str = "draw",
+    rng: Optional[np.random.Generator] = None,
+) -> Batch:
+    """Draw one batch.
+
+    ``seqs`` lists ``(cached, q_len)`` per sequence in packed order.
+    ``shared_groups`` lists ``(members, n_blocks)``: the first ``n_blocks``
+    logical blocks of every member point at the same physical blocks (a
+    read-only shared prefix; each member must hold at least that many full
+    cached blocks).  ``num_blocks`` defaults to ``ceil(pool_factor * used)``.
+    """
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
+    S = len(seqs)
+    cached = np.array([c for c, _ in seqs], dtype=np.int64)
+    qlen = np.array([n for _, n in seqs], dtype=np.int64)
+    if (cached < 0).any() or (qlen < 0).any():
+        raise ValueError("negative length")
+    seq_lens = cached + qlen
+    need = np.array([_blocks_needed(int(n)) for n in seq_lens], dtype=np.int64)
+
+    shared_of = {}
+    for gi, (members, nb) in enumerate(shared_groups):
+        for m in members:
+            if m in shared_of:
+                raise ValueError("sequence in two shared groups")
+            if cached[m] < nb * BLOCK_SIZE:
+                raise ValueError("shared prefix must be full cached blocks")
+            shared_of[m] = (gi, nb)
+    n_shared = sum(nb for _, nb in shared_groups)
+    used = int(need.sum()) - sum(shared_of[m][1] for m in shared_of) + n_shared
+    if num_blocks is None:
+        num_blocks = int(math.ceil(pool_factor * used))
+    if used > num_blocks:
+        raise ValueError(f"pool of {num_blocks} blocks cannot hold {used}")
+
+    perm = rng.permutation(num_blocks).astype(np.int64)
+    cursor = 0
+    group_blocks = []
+    for _, nb in shared_groups:
+        group_blocks.append(perm[cursor:cursor + nb])
+        cursor += nb
+    mb = max(1, int(need.max()) if S else 1)
+    bt = np.full((S, mb), -1, dtype=np.int64)
+    for s in range(S):
+        start = 0
+        if s in shared_of:
+            gi, nb = shared_of[s]
+            bt[s, :nb] = group_blocks[gi]
+            start = nb
+        n_priv = int(need[s]) - start
+        bt[s, start:start + n_priv] = perm[cursor:cursor + n_priv]
+        cursor += n_priv
+
+    T = int(qlen.sum())
+    cu = np.zeros(S + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(qlen)
+    q = bf16_normal(rng, (T, num_q_heads, head_dim))
+    k_new = bf16_normal(rng, (T, num_kv_heads, head_dim))
+    v_new = bf16_normal(rng, (T, num_kv_heads, head_dim))
+
+    tile = BLOCK_SIZE * head_dim
+    if pool == "skip":
+        k_pool = v_pool = None
+    else:
+        k_pool = np.empty((num_blocks, num_kv_heads, tile), dtype=np.uint16)
+        v_pool = np.empty((num_blocks, num_kv_heads, tile), dtype=np.uint16)
+        referenced = np.zeros(num_blocks, dtype=bool)
+        referenced[bt[bt >= 0]] = True
+        ref_ids = np.nonzero(referenced)[0]
+        k_pool[ref_ids] = bf16_normal(rng, (ref_ids.size, num_kv_heads, tile))
+        v_pool[ref_ids] = bf16_normal(rng, (ref_ids.size, num_kv_heads, tile))
+        free_ids = np.nonzero(~referenced)[0]
+        if unused_fill == "nan":
+            k_pool[free_ids] = QNAN_BF16
+            v_pool[free_ids] = QNAN_BF16
+        elif unused_fill == "zero":
+            k_pool[free_ids] = 0
+            v_pool[free_ids] = 0
+        elif unused_fill == "normal":
+            k_pool[free_ids] = bf16_normal(rng, (free_ids.size, num_kv_heads, tile))
+            v_pool[free_ids] = bf16_normal(rng, (free_ids.size, num_kv_heads, tile))
+        else:
+            raise ValueError(unused_fill)
+
+    return Batch(
+        name=name,
+        num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        cu_seqlens_q=cu.astype(np.int32),
+        seq_lens=seq_lens.astype(np.int32),
+        block_tables=bt.astype(np.int32),
+        num_blocks=int(num_blocks),
+        q=q,
+        k_new=k_new,
+        v_new=v_new,
+        k_pool=k_pool,
+        v_pool=v_pool,
+        scale=np.float32(1.0 / math.sqrt(head_dim)),
+        shared_groups=[(tuple(m), nb) for m, nb in shared_groups],
+        seed=seed,
+    )
+
+
+def permute_placement(batch: Batch, seed: int) -> Batch:
+    """Same logical K/V, new physical placement: whole tiles move to new block
+    ids and every block-table entry is renamed the same way."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    perm = rng.permutation(batch.num_blocks)
+    k_pool = np.empty_like(batch.k_pool)
+    v_pool = np.empty_like(batch.v_pool)
+    k_pool[perm] = batch.k_pool
+    v_pool[perm] = batch.v_pool
+    bt = batch.block_tables.astype(np.int64)
+    bt = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
+    return dataclasses.replace(batch, k_pool=k_pool, v_pool=v_pool,
+                               block_tables=bt.astype(np.int32))
+
+
+# ----------------------------------------------------------------------------
+# The single-step workloads.  Shapes follow the pages' Llama-3-8B figures
+# (32 query heads, 8 GQA KV heads, head_dim 128, bf16).
+# ----------------------------------------------------------------------------
+
+def config_worked_step(seed: int = CONFIG_SEEDS[1], **kw) -> Batch:
+    """The selective-batching worked step of "11.2 连续批处理与 PagedAttention"
+    (section 11.2.2): R1 prefills 5 tokens with nothing cached, R2 decodes
+    with 7 cached (8 visible), R3 decodes with 3 cached (4 visible); 7 packed
+    rows; a 64-block pool."""
+    return make_batch("worked-step-3req-7rows", [(0, 5), (7, 1), (3, 1)],
+                      seed=seed, num_blocks=64, **kw)
+
+
+def config_decode64(seed: int = CONFIG_SEEDS[2], **kw) -> Batch:
+    """Decode-only step: 64 sequences, one query row each, cached lengths
+    uniform integers in [128, 4096]; pool = ceil(1.25 x blocks used)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cached = rng.integers(128, 4096, size=64, endpoint=True)
+    return make_batch("decode-64seq-ctx128-4096", [(int(c), 1) for c in cached],
+                      seed=seed, rng=rng, **kw)
+
+
+def config_mixed_chunked(seed: int = CONFIG_SEEDS[3], n_decode: int = 1024, **kw) -> Batch:
+    """Mixed chunked-prefill step at a 2048-token budget: four 256-row prefill
+    chunks continuing cached prefixes of 0/1024/2048/3072 tokens, then 1024
+    decode rows whose cached lengths are log-normal (median 1024, sigma 1.0)
+    clipped to [16, 8192]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dec = np.clip(np.rint(np.exp(rng.normal(math.log(1024.0), 1.0, size=n_decode))), 16, 8192)
+    seqs = [(p, 256) for p in (0, 1024, 2048, 3072)] + [(int(c), 1) for c in dec]
+    return make_batch("mixed-4x256prefill-1024decode", seqs, seed=seed, rng=rng, **kw)
+
+
+def config_long_shared(seed: int = CONFIG_SEEDS[4], n_seqs: int = 16, cached: int = 32768,
+                       group: int = 8, shared_tokens: int = 2048, **kw) -> Batch:
+    """Long-context decode with prefix sharing: 16 sequences x 32768 cached
+    tokens, one query row each; each group of 8 sequences aliases the same
+    physical blocks for its first 2048 tokens."""
+    nb = shared_tokens // BLOCK_SIZE
+    groups = [(tuple(range(g, min(g + group, n_seqs))), nb) for g in range(0, n_seqs, group)]
+    return make_batch("longctx-16x32768-shared2048", [(cached, 1)] * n_seqs,
+                      seed=seed, shared_groups=groups, **kw)
