@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of one packed, ragged attention step over a paged KV cache on
+one MI355X.
+
+A step is the whole hot path on one synthetic batch resident in HBM: slot
+translation, KV append, the fused attention launch and the split merge
+(the same calls as pkv_paged_step, issued one by one so the attention
+launch can be bracketed with HIP events on its own stream).  The default
+workload is the decode-only step: 64 sequences, one query row each,
+cached contexts uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128,
+bf16.
+
+Prints ONE JSON line.  `value` is KV GB/s over the whole step (unique KV
+bytes / step time); query tok/s, the attention kernel's roofline fraction
+and the fp64 CPU oracle's rate on the same batch are reported beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "packed-step attention: KV GB/s + query tok/s vs HBM/MFMA roofline, 1 GPU"
+
+WORKLOADS = {
+    "decode64": "config_decode64",
+    "worked": "config_worked_step",
+    "mixed": "config_mixed_chunked",
+    "longshared": "config_long_shared",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this path has no "
+              "multi-GPU form: the step shards by sequence with no exchange.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_149_amd as pkv
+    from paged_kv_cache_149_amd import accounting
+    from synth import workloads as wl
+    from synth.device import to_device
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    pkv.load_library()
+    batch = getattr(wl, WORKLOADS[args.workload])()
+    log(f"workload {batch.name}: {batch.num_seqs} seqs, {batch.num_rows} rows, {batch.num_blocks} blocks")
+    t = to_device(batch, dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = pkv.pkv_plan(batch.cu_seqlens_q, batch.seq_lens, batch.num_q_heads, batch.num_kv_heads,
+                        batch.head_dim, block_tables=batch.block_tables, num_blocks=batch.num_blocks,
+                        device=dev, stream=stream)
+    slots = torch.empty(batch.num_rows, dtype=torch.int64, device=dev)
+    out = torch.empty_like(t["q"])
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        pkv.pkv_slot_mapping(t["cu_seqlens_q"], t["seq_lens"], t["block_tables"], t["num_blocks"],
+                             out=slots, stream=stream)
+        pkv.pkv_paged_kv_append(t["k_new"], t["v_new"], slots, t["k_cache"], t["v_cache"], stream=stream)
+        if i is not None:
+            ev[i][0].record(stream)
+        pkv.pkv_varlen_attention_main(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["scale"],
+                                      plan, out=out, stream=stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        pkv.pkv_split_kv_reduce(plan, out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    log(f"step {ms_step:.4f} ms, attention launch {attn_ms:.4f} ms")
+
+    nbytes = accounting.step_bytes(batch.cu_seqlens_q, batch.seq_lens, batch.block_tables,
+                                   batch.num_q_heads, batch.num_kv_heads, batch.head_dim)
+    flop = accounting.attention_flop(batch.cu_seqlens_q, batch.seq_lens, batch.num_q_heads, batch.head_dim)
+    kv_gbs = nbytes["kv_unique"] / (ms_step * 1e-3) / 1e9
+    attn_gbs = nbytes["total"] / (attn_ms * 1e-3) / 1e9
+    attn_tflops = flop / (attn_ms * 1e-3) / 1e12
+    hbm_bound = nbytes["total"] / (HBM_PEAK_GBS * 1e9) >= flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": "attention_kernel", "avg_ms": round(attn_ms, 5),
+                 "bytes_per_launch": nbytes["total"], "flop_per_launch": flop})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(batch, args.cpu_seconds, nbytes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": batch.name, "seqs": batch.num_seqs, "rows": batch.num_rows,
+                   "q_heads": batch.num_q_heads, "kv_heads": batch.num_kv_heads,
+                   "head_dim": batch.head_dim, "block_size": 16, "num_blocks": batch.num_blocks,
+                   "kv_keys": int(plan.kv_keys), "items": int(plan.num_items),
+                   "split_keys": int(plan.split_keys)},
+        "query_tok_s": round(batch.num_rows / (ms_step * 1e-3), 1),
+        "kv_bytes_unique": nbytes["kv_unique"],
+        "attention_flop": flop,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(batch, seconds, nbytes):
+    """The fp64 oracle, untuned, on the host cores: whole-batch passes of
+    the same step (inputs materialised first, outside the clock)."""
+    import oracle
+    from synth import workloads as wl
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = cores
+    log("cpu baseline: materialising the pool for the oracle")
+    import dataclasses
+    b = dataclasses.replace(batch, k_pool=_materialize_used(batch.k_pool, batch),
+                            v_pool=_materialize_used(batch.v_pool, batch))
+    reps, t_total = 0, 0.0
+    while t_total < seconds and reps < 100:
+        t0 = time.perf_counter()
+        oracle.packed_attention(b)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per = t_total / reps
+    log(f"cpu baseline: {reps} oracle passes, {per:.3f} s each")
+    return {"value": round(nbytes["kv_unique"] / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{reps} full passes of the same {batch.num_rows}-row step "
+                                        f"(fp64 numpy, {per:.3f} s per pass, host cores available: {cores})",
+            "query_tok_s": round(batch.num_rows / per, 2)}
+
+
+class _Dense:
+    """Pool view backed by a dict of materialised tiles (the blocks the
+    batch references), so the oracle's reads cost no generation time."""
+
+    def __init__(self, tiles, shape):
+        self.tiles, self.shape = tiles, shape
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            return self.tiles[int(key[0])][key[1]]
+        a = np.asarray(key)
+        if a.ndim == 0:
+            return self.tiles[int(a)]
+        return np.stack([self.tiles[int(x)] for x in a.reshape(-1)])
+
+
+def _materialize_used(pool, batch):
+    if isinstance(pool, np.ndarray):
+        return pool
+    used = np.unique(batch.block_tables[batch.block_tables >= 0])
+    arr = pool.tiles(used)
+    return _Dense({int(b): arr[i] for i, b in enumerate(used)}, pool.shape)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * pkv.h -- C ABI of libpkv: one packed, ragged attention step over a paged
+ * KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The step (one transformer layer's attention in one scheduler iteration):
+ *   1. slot translation: every packed query row gets the physical slot of its
+ *      position, slot = block_table[s][pos / 16] * 16 + pos % 16
+ *      ("连续批处理与 PagedAttention 原理", section "block table 与地址映射");
+ *   2. append: the step's new K/V rows are written into their slots
+ *      ("continuous batching" (k4i.top), section "与 KV cache 的关系": a chunk's
+ *      new KV entries are written to the cache, later chunks read them back);
+ *   3. plan: the ragged batch is cut into work items (decode rows split over
+ *      the key axis, prefill rows tiled over query positions), on the host;
+ *   4. attention: each row attends to its own request's keys under the
+ *      block-diagonal causal mask M_ij = 0 iff req(i) = req(j) and j <= i
+ *      ("continuous batching" (k4i.top), section "防止跨请求 attention"),
+ *      out = softmax(scale * q K^T + M) V, with the request boundaries given
+ *      by cu_seqlens of shape [requests + 1] ("11.2 连续批处理与 PagedAttention",
+ *      section 11.2.2) and GQA: query head h reads kv head h / (Hq / Hkv);
+ *   5. merge: key-split partial results are combined (log-sum-exp merge).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless the name starts with h_ (host).
+ * - The caller owns every buffer; the library never allocates or frees
+ *   device or host memory and keeps no state between calls.
+ * - bf16 tensors are passed as pkv_bf16 (the 16-bit pattern).
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every device call is
+ *   asynchronous on that stream; the return value only reports host-side
+ *   argument validation and launch errors.
+ * - Integer metadata is int32; slots are int64.
+ * - Supported shapes: head_dim 128, block size 16, Hq % Hkv == 0 with
+ *   Hq / Hkv in {1, 2, 4, 8, 16}.  Anything else returns PKV_EUNSUPPORTED.
+ *
+ * Paged pool layout (the pages fix only the slot translation and that a
+ * block's 16 tokens are contiguous; they leave the tensor layout open):
+ *   k_cache : bf16[num_blocks][Hkv][16][128]   token-major 4 KiB tiles
+ *   v_cache : bf16[num_blocks][Hkv][128][16]   dimension-major 4 KiB tiles
+ * Slot x is block x / 16, offset x % 16.  Key element (o, d) of a tile sits
+ * at o * 128 + d; value element (o, d) at d * 16 + o.
+ *
+ * Packed tensors:
+ *   q        : bf16[T][Hq][128]      k_new, v_new : bf16[T][Hkv][128]
+ *   out      : bf16[T][Hq][128]      slot_mapping : int64[T]
+ *   cu_seqlens_q : int32[S + 1], cu[0] = 0, non-decreasing, cu[S] = T
+ *   seq_lens : int32[S], keys visible to the sequence's last row AFTER this
+ *              step's rows are appended (cached prefix + q_len); row j of
+ *              sequence s sits at position seq_lens[s] - q_len_s + j
+ *   block_tables : int32[S][bt_stride]; entries past the sequence's last
+ *              needed block (ceil(seq_lens[s] / 16)) are never read.
+ * Sequences with q_len = 0 are allowed and contribute nothing.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pkv_bf16;
+typedef void *pkv_stream_t; /* hipStream_t */
+
+#define PKV_BLOCK_SIZE 16
+#define PKV_HEAD_DIM 128
+#define PKV_ITEM_INTS 8
+#define PKV_MERGE_INTS 4
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* malformed argument (null pointer, bad metadata) */
+  PKV_ERANGE = 2,        /* a size or index does not fit (e.g. block id) */
+  PKV_EUNSUPPORTED = 3,  /* head_dim / GQA ratio outside the supported set */
+  PKV_EWORKSPACE = 4,    /* workspace or host staging buffer too small */
+  PKV_EHIP = 5           /* the HIP runtime reported an error */
+};
+
+/* Static description of a status code. */
+const char *pkv_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int pkv_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Slot translation ("连续批处理与 PagedAttention 原理", section "block table
+ * 与地址映射": logical block p / 16 -> physical block b -> offset b*16 + p%16).
+ * For every packed row t of sequence s at position pos:
+ *   slot_mapping[t] = block_tables[s * bt_stride + pos / 16] * 16 + pos % 16
+ * A row whose table entry is outside [0, num_blocks) gets slot -1 (the append
+ * then skips it).  Errors: PKV_EINVAL for null pointers or negative sizes,
+ * PKV_EHIP on launch failure.  Metadata is not otherwise validated on the
+ * device; validate it on the host with pkv_plan.
+ * ------------------------------------------------------------------------- */
+int pkv_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                     const int32_t *block_tables, int32_t bt_stride,
+                     int32_t num_seqs, int32_t num_rows, int64_t num_blocks,
+                     int64_t *slot_mapping, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged KV append ("continuous batching" (k4i.top), section "与 KV cache 的关
+ * 系"; "11.2 连续批处理与 PagedAttention", section 11.2.2: the new K and V are
+ * appended to their request's cache).  Bit-exact copy of k_new[t] and
+ * v_new[t] (all kv heads) into slot slot_mapping[t] of k_cache / v_cache in
+ * the layout above.  Rows whose slot is negative or >= num_blocks * 16 are
+ * skipped.  Two rows with the same slot race (undefined).  Errors as for
+ * pkv_slot_mapping.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                        const int64_t *slot_mapping, int32_t num_rows,
+                        pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                        int64_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Work partitioning (host).  Decode rows ("11.2 连续批处理与 PagedAttention",
+ * section 11.2.2: attention runs per request inside one launch) become items
+ * (sequence, kv head, key range); long contexts are split over the key axis
+ * so the launch fills the chip, and split results are merged afterwards.
+ * Rows of sequences with q_len > 1 (prefill and chunked prefill, whose
+ * causal offset is the cached prefix: "Continuous Batching 深入实现", section
+ * "一个 chunked prefill 请求怎么组织 attention") become tiles of query
+ * positions x the kv head's query heads.  Wide tiles come first in the list,
+ * then everything else longest-first.
+ *
+ * The plan is written to h_staging (host memory; pinned memory lets the copy
+ * run asynchronously) and, when ws is not NULL, copied to ws with
+ * hipMemcpyAsync on `stream`.  h_staging must stay untouched until that copy
+ * has executed.  One plan serves every layer of a step (same metadata).
+ *
+ * Size query: with h_staging == NULL the call only fills plan->ws_bytes and
+ * plan->host_bytes.  With ws == NULL the plan is built on the host only.
+ * Validation (host copies): cu[0] == 0, cu non-decreasing, num_rows = cu[S],
+ * 0 <= q_len_s <= seq_lens[s]; with h_block_tables given, every entry a
+ * sequence needs must lie in [0, num_blocks).  Errors: PKV_EINVAL,
+ * PKV_ERANGE, PKV_EUNSUPPORTED, PKV_EWORKSPACE (plan->ws_bytes /
+ * plan->host_bytes then hold the sizes needed), PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_plan_options {
+  int32_t target_items;   /* aim for about this many items (0 = default) */
+  int32_t min_split_keys; /* shortest key split, multiple of 32 (0 = default) */
+  int32_t wide_tiles;     /* -1 auto, 0 never, 1 always use wide prefill tiles */
+  int32_t reserved;
+} pkv_plan_options_t;
+
+typedef struct pkv_plan {
+  int32_t num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim;
+  int32_t num_items;      /* attention work items */
+  int32_t num_wide_items; /* items with wide (64-column) tiles, at the front */
+  int32_t num_merge;      /* merge entries (one per split output row x head) */
+  int32_t num_part_cols;  /* partial-result columns in the workspace */
+  int32_t split_keys;     /* key-split length chosen for split items */
+  int64_t items_off, merge_off, ml_off, o_off; /* byte offsets into ws */
+  size_t ws_bytes;        /* workspace bytes this plan uses */
+  size_t host_bytes;      /* host staging bytes this plan uses */
+  int64_t kv_keys;        /* sum over sequences of visible keys (accounting) */
+  int64_t visible_pairs;  /* sum over rows of visible keys (accounting) */
+} pkv_plan_t;
+
+int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
+             int32_t num_seqs, int32_t num_rows, int32_t num_q_heads,
+             int32_t num_kv_heads, int32_t head_dim,
+             const int32_t *h_block_tables, int32_t bt_stride,
+             int64_t num_blocks, const pkv_plan_options_t *opts,
+             void *h_staging, size_t h_staging_bytes, void *ws,
+             size_t ws_bytes, pkv_plan_t *plan, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused varlen paged attention, main launch.  One grid walks the plan's
+ * items; decode items and prefill tiles share the launch.  For each row t
+ * of sequence s at position pos and query head h:
+ *   out[t][h] = sum_{i <= pos} softmax_i(scale * q[t][h] . K_s[i][g]) V_s[i][g]
+ * with g = h / (Hq / Hkv) and K_s / V_s read from the pool through the
+ * block table ("continuous batching" (k4i.top), section "与 KV cache 的关系",
+ * the decode formula with [K_cache; k_t]; visible set of section "为什么
+ * packed forward 等价").  Rows whose keys were split write fp32 partial
+ * results (running max, sum, unnormalised output) into ws; every other row
+ * writes out directly.  Accumulation is fp32; probabilities are rounded to
+ * bf16 for the P.V product and the normaliser sums those rounded values;
+ * out is rounded to bf16 (nearest even).  Block-table entries outside
+ * [0, num_blocks) read as zero keys/values.  Errors: PKV_EINVAL (null
+ * pointers, plan mismatch), PKV_EWORKSPACE, PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
+                              const pkv_bf16 *v_cache,
+                              const int32_t *block_tables, int32_t bt_stride,
+                              int64_t num_blocks, float scale,
+                              const pkv_plan_t *plan, void *ws, size_t ws_bytes,
+                              pkv_bf16 *out, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Split-KV merge: for every row and head whose keys were split,
+ *   M = max_k m_k,  out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
+ * (m_k in the base-2 scaled domain of the main launch), rounded to bf16.
+ * The pages do not describe this step; it is the standard online-softmax
+ * combination and changes nothing but rounding.  A plan with no split rows
+ * launches nothing.  Errors as above.
+ * ------------------------------------------------------------------------- */
+int pkv_split_kv_reduce(const pkv_plan_t *plan, const void *ws,
+                        size_t ws_bytes, pkv_bf16 *out, pkv_stream_t stream);
+
+/* pkv_varlen_attention_main followed by pkv_split_kv_reduce. */
+int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
+                               const pkv_bf16 *v_cache,
+                               const int32_t *block_tables, int32_t bt_stride,
+                               int64_t num_blocks, float scale,
+                               const pkv_plan_t *plan, void *ws,
+                               size_t ws_bytes, pkv_bf16 *out,
+                               pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The whole step on one stream: slot translation into slot_mapping (device
+ * int64[T], written), append, attention, merge.  Attention reads the cache
+ * after the append, so each row sees its own new key.
+ * ------------------------------------------------------------------------- */
+int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
+                   const pkv_bf16 *v_new, pkv_bf16 *k_cache,
+                   pkv_bf16 *v_cache, const int32_t *cu_seqlens_q,
+                   const int32_t *seq_lens, const int32_t *block_tables,
+                   int32_t bt_stride, int64_t num_blocks,
+                   int64_t *slot_mapping, float scale, const pkv_plan_t *plan,
+                   void *ws, size_t ws_bytes, pkv_bf16 *out,
+                   pkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

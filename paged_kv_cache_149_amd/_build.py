@@ -1,0 +1,57 @@
+"""Build libpkv.so in-tree with hipcc for gfx950.
+
+Every call compiles from source.  The library is written to a temporary
+name and renamed into place, so a half-written file is never loaded.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libpkv.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["pkv_kernels.hip", "pkv_plan.cpp"]
+
+# -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    cc = hipcc()
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    fd, tmp = tempfile.mkstemp(prefix=".libpkv.", suffix=".so.tmp", dir=HERE)
+    os.close(fd)
+    cmd = [cc, *DEVICE_FLAGS, *COMMON_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
+           "-shared", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+        if verbose and res.stderr.strip():
+            print(res.stderr, flush=True)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,316 @@
+"""ctypes binding of libpkv (include/pkv.h).  Argument marshalling only:
+every step of the path runs in the library's HIP kernels.
+
+The library must be built (``python -m paged_kv_cache_149_amd._build`` or
+``__graft_entry__.build()``); there is no fallback.  torch is imported before
+the library is loaded so that both use the one HIP runtime already in the
+process (libamdhip64.so.7), which makes torch's device pointers and stream
+handles valid arguments.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._build import LIB_PATH, INCLUDE
+
+BLOCK_SIZE = 16
+HEAD_DIM = 128
+ITEM_INTS = 8
+MERGE_INTS = 4
+
+PKV_OK = 0
+_STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_ERANGE", 3: "PKV_EUNSUPPORTED",
+           4: "PKV_EWORKSPACE", 5: "PKV_EHIP"}
+
+
+class PKVError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        self.status = status
+        super().__init__(f"{func} failed: {_STATUS.get(status, status)}")
+
+
+class PlanOptions(ctypes.Structure):
+    _fields_ = [("target_items", ctypes.c_int32), ("min_split_keys", ctypes.c_int32),
+                ("wide_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class PlanStruct(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_items", ctypes.c_int32),
+                ("num_wide_items", ctypes.c_int32), ("num_merge", ctypes.c_int32),
+                ("num_part_cols", ctypes.c_int32), ("split_keys", ctypes.c_int32),
+                ("items_off", ctypes.c_int64), ("merge_off", ctypes.c_int64),
+                ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
+                ("ws_bytes", ctypes.c_size_t), ("host_bytes", ctypes.c_size_t),
+                ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (ctypes.c_int, []),
+    "pkv_slot_mapping": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I64, _P, _P]),
+    "pkv_paged_kv_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _P]),
+    "pkv_plan": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I64,
+                                ctypes.POINTER(PlanOptions), _P, _SZ, _P, _SZ,
+                                ctypes.POINTER(PlanStruct), _P]),
+    "pkv_varlen_attention_main": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _F,
+                                                 ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_split_kv_reduce": (ctypes.c_int, [ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _F,
+                                                  ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_paged_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
+                                      ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/pkv.h declares."""
+    txt = open(os.path.join(INCLUDE, "pkv.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pkv_\w+)\s*\(", txt, flags=re.M)))
+
+
+def _check(name: str, status: int):
+    if status != PKV_OK:
+        raise PKVError(name, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and (t.device.type != "cuda" or (dev.index is not None and t.device != dev)):
+        raise ValueError(f"{name} must live on {dev}")
+
+
+# ---------------------------------------------------------------------------
+# host <-> device helpers for bf16 bit patterns
+# ---------------------------------------------------------------------------
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """bf16 tensor on ``device`` from uint16 bit patterns."""
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor (copied to the host)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def pkv_slot_mapping(cu_seqlens_q, seq_lens, block_tables, num_blocks, out=None, stream=None):
+    lib = load_library()
+    dev = cu_seqlens_q.device
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seq_lens", seq_lens), ("block_tables", block_tables)):
+        _need(t, n, torch.int32, dev)
+    S = seq_lens.shape[0]
+    T = int(cu_seqlens_q[-1].item()) if out is None else out.shape[0]
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=dev)
+    _need(out, "slot_mapping", torch.int64, dev)
+    _check("pkv_slot_mapping", lib.pkv_slot_mapping(
+        _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], S, T,
+        int(num_blocks), _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def pkv_paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+    lib = load_library()
+    dev = k_cache.device
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, n, torch.bfloat16, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    T, Hkv, D = k_new.shape
+    nb = k_cache.shape[0]
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
+        raise ValueError("row counts differ")
+    _check("pkv_paged_kv_append", lib.pkv_paged_kv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), nb, Hkv, D,
+        _stream(stream, dev)))
+
+
+class Plan:
+    """A work plan in a device workspace.  Keeps its pinned host staging
+    buffer alive (and its copy event) as long as the plan lives."""
+
+    def __init__(self, st: PlanStruct, workspace: torch.Tensor, staging: torch.Tensor, event):
+        self.st = st
+        self.workspace = workspace
+        self.staging = staging
+        self.event = event
+
+    def __getattr__(self, k):
+        return getattr(self.st, k)
+
+    def items(self) -> np.ndarray:
+        n = self.st.num_items
+        return self.staging[:n * ITEM_INTS * 4].numpy().view(np.int32).reshape(n, ITEM_INTS).copy()
+
+    def merges(self) -> np.ndarray:
+        n = self.st.num_merge
+        off = self.st.merge_off
+        return self.staging[off:off + n * MERGE_INTS * 4].numpy().view(np.int32).reshape(n, MERGE_INTS).copy()
+
+
+def pkv_plan(cu_seqlens_q: np.ndarray, seq_lens: np.ndarray, num_q_heads: int, num_kv_heads: int,
+             head_dim: int = HEAD_DIM, block_tables: Optional[np.ndarray] = None,
+             num_blocks: int = 0, options: Optional[dict] = None, device=None,
+             workspace: Optional[torch.Tensor] = None, stream=None, host_only: bool = False) -> Plan:
+    """Build the work plan from HOST copies of the metadata.  With
+    host_only=True nothing touches a GPU (the plan stays in host memory)."""
+    lib = load_library()
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    S = sl.shape[0]
+    T = int(cu[-1]) if cu.size else 0
+    bt = None if block_tables is None else np.ascontiguousarray(block_tables, dtype=np.int32)
+    opts = PlanOptions(**(options or {"wide_tiles": -1}))
+    if options is not None and "wide_tiles" not in options:
+        opts.wide_tiles = -1
+    st = PlanStruct()
+    args = [cu.ctypes.data_as(_P), sl.ctypes.data_as(_P), S, T, num_q_heads, num_kv_heads, head_dim,
+            None if bt is None else bt.ctypes.data_as(_P), 0 if bt is None else bt.shape[1],
+            int(num_blocks), ctypes.byref(opts)]
+    _check("pkv_plan", lib.pkv_plan(*args, None, 0, None, 0, ctypes.byref(st), None))
+    host_bytes = max(int(st.host_bytes), 1)
+    if host_only:
+        staging = torch.empty(host_bytes, dtype=torch.uint8)
+        _check("pkv_plan", lib.pkv_plan(*args, _P(staging.data_ptr()), host_bytes, None, 0,
+                                         ctypes.byref(st), None))
+        return Plan(st, None, staging, None)
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    staging = torch.empty(host_bytes, dtype=torch.uint8, pin_memory=True)
+    need = max(int(st.ws_bytes), 256)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    _check("pkv_plan", lib.pkv_plan(*args, _P(staging.data_ptr()), host_bytes,
+                                     _P(workspace.data_ptr()), workspace.numel(),
+                                     ctypes.byref(st), ctypes.c_void_p(s.cuda_stream)))
+    ev = torch.cuda.Event()
+    ev.record(s)
+    return Plan(st, workspace, staging, ev)
+
+
+def _attn_args(q, k_cache, v_cache, block_tables, plan: Plan, out):
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    T, Hq, D = q.shape
+    if T != plan.st.num_rows or Hq != plan.st.num_q_heads or D != plan.st.head_dim:
+        raise ValueError("q does not match the plan")
+    nb, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if Hkv != plan.st.num_kv_heads:
+        raise ValueError("kv heads do not match the plan")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if block_tables.shape[0] != plan.st.num_seqs:
+        raise ValueError("block_tables rows do not match the plan")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, dev)
+    if out.shape != q.shape:
+        raise ValueError("out shape")
+    return dev, nb, out
+
+
+def pkv_varlen_attention_main(q, k_cache, v_cache, block_tables, scale, plan: Plan, out=None, stream=None):
+    lib = load_library()
+    dev, nb, out = _attn_args(q, k_cache, v_cache, block_tables, plan, out)
+    ws = plan.workspace
+    _check("pkv_varlen_attention_main", lib.pkv_varlen_attention_main(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], nb,
+        float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def pkv_split_kv_reduce(plan: Plan, out, stream=None):
+    lib = load_library()
+    _need(out, "out", torch.bfloat16, out.device)
+    ws = plan.workspace
+    _check("pkv_split_kv_reduce", lib.pkv_split_kv_reduce(
+        ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, out.device)))
+    return out
+
+
+def pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, scale, plan: Plan, out=None, stream=None):
+    lib = load_library()
+    dev, nb, out = _attn_args(q, k_cache, v_cache, block_tables, plan, out)
+    ws = plan.workspace
+    _check("pkv_paged_varlen_attention", lib.pkv_paged_varlen_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], nb,
+        float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, scale,
+                   plan: Plan, slot_mapping=None, out=None, stream=None):
+    lib = load_library()
+    dev, nb, out = _attn_args(q, k_cache, v_cache, block_tables, plan, out)
+    _need(k_new, "k_new", torch.bfloat16, dev)
+    _need(v_new, "v_new", torch.bfloat16, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    if slot_mapping is None:
+        slot_mapping = torch.empty(q.shape[0], dtype=torch.int64, device=dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    ws = plan.workspace
+    _check("pkv_paged_step", lib.pkv_paged_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+        _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], nb, _ptr(slot_mapping),
+        float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
+    return out, slot_mapping

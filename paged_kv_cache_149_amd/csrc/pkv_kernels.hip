@@ -1,0 +1,531 @@
+// HIP kernels for one packed, ragged attention step over a paged KV cache,
+// written for CDNA4 (gfx950, wave64, bf16 MFMA).
+//
+//   slot_mapping_kernel  slot translation b*16 + p%16
+//                        ("连续批处理与 PagedAttention 原理", "block table 与地址映射")
+//   kv_append_kernel     bit copy of the step's new K/V rows into their slots
+//   attention_kernel     fused decode + prefill tiles over the plan's items
+//   merge_kernel         log-sum-exp merge of key-split partial results
+//
+// Attention, per item (one wavefront): a tile of query columns (positions x
+// the GQA group's query heads, all reading the same kv head) against a key
+// range of one sequence, 32 keys (two paged blocks) per step:
+//   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, M = keys, N = columns, K = dims)
+//   online softmax per column in the base-2 domain, fp32
+//   O^T += V^T P^T (same MFMA, M = dims, N = columns, K = keys)
+// Operand layouts of the 16x16x32 MFMA (lane l, r = l % 16, g = l / 16):
+//   A[m][k]: lane holds A[r][8g .. 8g+7];  B[k][n]: lane holds B[8g .. 8g+7][r]
+//   C[m][n]: lane holds C[4g .. 4g+3][r]
+// Keys are assigned to the rows of the two S^T tiles so that lane group g's
+// eight C values are keys 8g .. 8g+7 of the step, exactly the slots it needs
+// as the B operand (P^T) of the P.V product.  The V tile of a block is
+// stored dimension-major (16 tokens contiguous per dimension), so the V^T A
+// operand is one 16-byte load per lane; K tiles are token-major and the K A
+// operand is one 16-byte load per lane per 32 dimensions.  No LDS, no
+// transposes: every operand comes straight from HBM in its MFMA layout.
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv::Item;
+using pkv::Merge;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = pkv::kHeadDim;
+constexpr int TILE = pkv::kBlock * pkv::kHeadDim;  // elements of a (block, head) tile
+
+__device__ inline float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ inline u32x4 load16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// fp32 -> bf16 (round to nearest even), packed two per dword; low half first
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ inline float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ inline float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// slot translation
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T,
+    int64_t num_blocks, int64_t *__restrict__ slots) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  // last s with cu[s] <= t (cu[S] = T > t)
+  int lo = 0, hi = S;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo < S ? lo : S - 1;
+  const int ql = cu[s + 1] - cu[s];
+  const int pos = seq_lens[s] - ql + (t - cu[s]);
+  int64_t slot = -1;
+  if (pos >= 0 && (pos >> 4) < bt_stride) {
+    const int b = bt[(int64_t)s * bt_stride + (pos >> 4)];
+    if (b >= 0 && b < num_blocks) slot = (int64_t)b * pkv::kBlock + (pos & 15);
+  }
+  slots[t] = slot;
+}
+
+// ---------------------------------------------------------------------------
+// append: one thread per (row, kv head, 8 dimensions)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    const int64_t *__restrict__ slots, int32_t T, int32_t Hkv, int64_t num_blocks,
+    uint16_t *__restrict__ kc, uint16_t *__restrict__ vc) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)Hkv * (D / 8);
+  if (idx >= (int64_t)T * per_row) return;
+  const int t = (int)(idx / per_row);
+  const int rem = (int)(idx - (int64_t)t * per_row);
+  const int h = rem / (D / 8);
+  const int d0 = (rem % (D / 8)) * 8;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * pkv::kBlock) return;
+  const int64_t b = slot >> 4;
+  const int o = (int)(slot & 15);
+  const int64_t src = ((int64_t)t * Hkv + h) * D + d0;
+  const int64_t tile = (b * Hkv + h) * TILE;
+  *reinterpret_cast<u32x4 *>(kc + tile + o * D + d0) = load16(k_new + src);
+  const u32x4 v = load16(v_new + src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vc[tile + (d0 + 2 * i) * pkv::kBlock + o] = (uint16_t)(v[i] & 0xFFFF);
+    vc[tile + (d0 + 2 * i + 1) * pkv::kBlock + o] = (uint16_t)(v[i] >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const uint16_t *q;
+  const uint16_t *kc;
+  const uint16_t *vc;
+  const int32_t *bt;
+  uint16_t *out;
+  const Item *items;
+  float2 *part_ml;
+  float *part_o;
+  int64_t num_blocks;
+  int32_t bt_stride;
+  int32_t num_items;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t log2G;
+  float scale_log2;  // scale * log2(e)
+};
+
+struct Chunk {
+  u32x4 k[8];  // [m-tile][32-dim step]
+  u32x4 v[8];  // [16-dim tile]
+};
+
+// Run one item with NT column tiles of 16 (NT = 1: up to 16 columns, NT = 4:
+// up to 64).  Everything indexed [nt] is per column tile.
+template <int NT>
+__device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = 1 << a.log2G;
+  const int Hq = a.Hq;
+
+  // ---- columns owned by this lane: column r of each tile
+  bool col_ok[NT];
+  int col_pos[NT];
+  int64_t col_qoff[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = nt * 16 + r;
+    const int pc = col >> a.log2G;
+    const int ho = col & (G - 1);
+    col_ok[nt] = pc < it.np;
+    col_pos[nt] = it.pos0 + pc;
+    col_qoff[nt] = ((int64_t)(it.t0 + pc) * Hq + it.kvh * G + ho) * D;
+  }
+
+  // ---- Q^T operand (B of S^T = K Q^T): dims 32c + 8g .. +7 of column r
+  u32x4 qb[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[nt][c] = col_ok[nt] ? load16(a.q + col_qoff[nt] + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+
+  f32x4 acc[NT][8];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = neg_inf();
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- block-table window: lane i holds entry (first block + base + i)
+  const int32_t *btrow = a.bt + (int64_t)it.seq * a.bt_stride;
+  const int kb0 = it.k0 >> 4;
+  // blocks of the item, never past the table row
+  const int nkb = min(((it.k1 + 15) >> 4), a.bt_stride) - kb0;
+  int bt_base = 0;
+  int btv = lane < nkb ? btrow[kb0 + lane] : -1;
+
+  const int nchunks = (it.k1 - it.k0 + 31) >> 5;
+  const int64_t head_off = (int64_t)it.kvh * TILE;
+  const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+
+  // per-lane constant parts of the operand addresses
+  const int ka = r >> 2, kbb = r & 3;               // K row r -> key 8*ka + 4*mt + kbb
+  const int k_sel = ka >> 1;                         // which block of the pair
+  const int k_row_off = (8 * (ka & 1) + kbb) * D + 8 * g;  // + 4*mt*D + 32*c
+  const int v_sel = g >> 1;
+  const int v_off = r * pkv::kBlock + 8 * (g & 1);         // + 16*dt*16
+
+  auto load_chunk = [&](int cc, Chunk &ch) {
+    const int rel0 = 2 * cc;
+    if (rel0 + 1 - bt_base >= 64) {  // slide the table window (uniform)
+      bt_base += 64;
+      btv = lane < nkb - bt_base ? btrow[kb0 + bt_base + lane] : -1;
+    }
+    const int key0 = it.k0 + 32 * cc;
+    const int b0 = __builtin_amdgcn_readlane(btv, rel0 - bt_base);
+    const bool need1 = key0 + 16 < it.k1;
+    const int b1 = need1 ? __builtin_amdgcn_readlane(btv, rel0 + 1 - bt_base) : -1;
+    const bool ok0 = b0 >= 0 && b0 < a.num_blocks;
+    const bool ok1 = b1 >= 0 && b1 < a.num_blocks;
+    const int64_t t0 = ok0 ? (int64_t)b0 * blk_stride + head_off : 0;
+    const int64_t t1 = ok1 ? (int64_t)b1 * blk_stride + head_off : 0;
+    const bool kok = k_sel ? ok1 : ok0;
+    const uint16_t *kp = a.kc + (k_sel ? t1 : t0) + k_row_off;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        ch.k[mt * 4 + c] = kok ? load16(kp + 4 * mt * D + 32 * c) : u32x4{0, 0, 0, 0};
+    const bool vok = v_sel ? ok1 : ok0;
+    const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      ch.v[dt] = vok ? load16(vp + dt * 16 * pkv::kBlock) : u32x4{0, 0, 0, 0};
+  };
+
+  auto compute_chunk = [&](int cc, Chunk &ch) {
+    const int key0 = it.k0 + 32 * cc;
+    const int kl = key0 + 8 * g;  // key of this lane's slot 0
+    if (key0 + 32 > it.k1) {
+      // keys past the range may hold stale data: zero their V so 0 * garbage
+      // cannot reach the accumulator
+      const int nv = it.k1 - kl;
+      u32x4 keep;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) ch.v[dt] &= keep;
+    }
+    u32x4 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s0 = mfma(ch.k[c], qb[nt][c], s0);
+        s1 = mfma(ch.k[4 + c], qb[nt][c], s1);
+      }
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = s0[i] * a.scale_log2;
+        sv[4 + i] = s1[i] * a.scale_log2;
+      }
+      float mx = neg_inf();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kl + j;
+        const bool ok = col_ok[nt] && key < it.k1 && key <= col_pos[nt];
+        sv[j] = ok ? sv[j] : neg_inf();
+        mx = fmaxf(mx, sv[j]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[nt], mx);
+      const float m_use = m_new == neg_inf() ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(sv[2 * i] - m_use),
+                                     __builtin_amdgcn_exp2f(sv[2 * i + 1] - m_use));
+        pb[nt][i] = w;
+        lsum += bf16_lo(w) + bf16_hi(w);
+      }
+      l_run[nt] = l_run[nt] * alpha + lsum;
+      m_run[nt] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(ch.v[dt], pb[nt], acc[nt][dt]);
+  };
+
+  // ---- main loop, one chunk of loads in flight ahead of the math
+  Chunk bufA, bufB;
+  load_chunk(0, bufA);
+  int cc = 0;
+  for (; cc + 2 <= nchunks; cc += 2) {
+    load_chunk(cc + 1, bufB);
+    compute_chunk(cc, bufA);
+    if (cc + 2 < nchunks) load_chunk(cc + 2, bufA);
+    compute_chunk(cc + 1, bufB);
+  }
+  if (cc < nchunks) compute_chunk(cc, bufA);
+
+  // ---- epilogue
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!col_ok[nt]) continue;
+    const int col = nt * 16 + r;
+    if (it.part < 0) {
+      const float inv = 1.f / l_tot;
+      uint16_t *op = a.out + col_qoff[nt] + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = acc[nt][dt] * inv;
+        u32x2 w;
+        w[0] = pack_bf16(v[0], v[1]);
+        w[1] = pack_bf16(v[2], v[3]);
+        *reinterpret_cast<u32x2 *>(op + 16 * dt) = w;
+      }
+    } else {
+      const int64_t pcol = (int64_t)it.part + col;
+      float *po = a.part_o + pcol * D + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4 *>(po + 16 * dt) = acc[nt][dt];
+      if (g == 0) a.part_ml[pcol] = make_float2(m_run[nt], l_tot);
+    }
+  }
+}
+
+template <bool kWide>
+__global__ __launch_bounds__(64) void attention_kernel(AttnArgs a) {
+  const int idx = blockIdx.x;
+  if (idx >= a.num_items) return;
+  Item it;
+  const int32_t *src = reinterpret_cast<const int32_t *>(a.items + idx);
+  it.seq = __builtin_amdgcn_readfirstlane(src[0]);
+  it.kvh = __builtin_amdgcn_readfirstlane(src[1]);
+  it.t0 = __builtin_amdgcn_readfirstlane(src[2]);
+  it.np = __builtin_amdgcn_readfirstlane(src[3]);
+  it.pos0 = __builtin_amdgcn_readfirstlane(src[4]);
+  it.k0 = __builtin_amdgcn_readfirstlane(src[5]);
+  it.k1 = __builtin_amdgcn_readfirstlane(src[6]);
+  it.part = __builtin_amdgcn_readfirstlane(src[7]);
+  if (it.k1 <= it.k0 || it.np <= 0) return;
+  if (kWide && (it.np << a.log2G) > pkv::kTileCols)
+    run_item<4>(a, it);
+  else
+    run_item<1>(a, it);
+}
+
+// ---------------------------------------------------------------------------
+// merge of key-split partials: one wavefront per (row, head); lane l owns
+// dimensions 2l, 2l+1
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void merge_kernel(const Merge *__restrict__ merges, int32_t n,
+                                                   const float2 *__restrict__ ml,
+                                                   const float *__restrict__ po,
+                                                   uint16_t *__restrict__ out) {
+  const int idx = blockIdx.x;
+  if (idx >= n) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t *e = reinterpret_cast<const int32_t *>(merges + idx);
+  const int out_row = __builtin_amdgcn_readfirstlane(e[0]);
+  const int first = __builtin_amdgcn_readfirstlane(e[1]);
+  const int nsplit = __builtin_amdgcn_readfirstlane(e[2]);
+  const int stride = __builtin_amdgcn_readfirstlane(e[3]);
+  float M = neg_inf();
+  for (int k = 0; k < nsplit; ++k) M = fmaxf(M, ml[first + (int64_t)k * stride].x);
+  float ax = 0.f, ay = 0.f, L = 0.f;
+  for (int k = 0; k < nsplit; ++k) {
+    const int64_t col = first + (int64_t)k * stride;
+    const float2 mlk = ml[col];
+    const float w = __builtin_amdgcn_exp2f(mlk.x - M);
+    const float2 o = *reinterpret_cast<const float2 *>(po + col * D + 2 * lane);
+    L += w * mlk.y;
+    ax += w * o.x;
+    ay += w * o.y;
+  }
+  const float inv = 1.f / L;
+  reinterpret_cast<uint32_t *>(out + (int64_t)out_row * D)[lane] = pack_bf16(ax * inv, ay * inv);
+}
+
+inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s); }
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP; }
+
+int check_plan(const pkv_plan_t *plan, size_t ws_bytes, const void *ws) {
+  if (!plan) return PKV_EINVAL;
+  if (plan->head_dim != D || plan->num_q_heads <= 0 || plan->num_kv_heads <= 0) return PKV_EINVAL;
+  if (plan->num_items > 0 && !ws) return PKV_EINVAL;
+  if (ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
+  return PKV_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_ERANGE: return "value out of range";
+    case PKV_EUNSUPPORTED: return "unsupported shape";
+    case PKV_EWORKSPACE: return "workspace too small";
+    case PKV_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pkv_version(void) { return 100; }
+
+int pkv_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                     const int32_t *block_tables, int32_t bt_stride, int32_t num_seqs,
+                     int32_t num_rows, int64_t num_blocks, int64_t *slot_mapping,
+                     pkv_stream_t stream) {
+  if (num_seqs < 0 || num_rows < 0 || bt_stride < 0) return PKV_EINVAL;
+  if (num_rows == 0) return PKV_OK;
+  if (num_seqs == 0 || !cu_seqlens_q || !seq_lens || !block_tables || !slot_mapping)
+    return PKV_EINVAL;
+  const int grid = (num_rows + 255) / 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(grid), dim3(256), 0, as_stream(stream),
+                     cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs, num_rows,
+                     num_blocks, slot_mapping);
+  return launch_status();
+}
+
+int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                        const int64_t *slot_mapping, int32_t num_rows, pkv_bf16 *k_cache,
+                        pkv_bf16 *v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, pkv_stream_t stream) {
+  if (num_rows < 0 || num_kv_heads <= 0 || num_blocks < 0) return PKV_EINVAL;
+  if (head_dim != D) return PKV_EUNSUPPORTED;
+  if (num_rows == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  const int64_t total = (int64_t)num_rows * num_kv_heads * (D / 8);
+  const int64_t grid = (total + 255) / 256;
+  if (grid > INT32_MAX) return PKV_ERANGE;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                     k_new, v_new, slot_mapping, num_rows, num_kv_heads, num_blocks, k_cache,
+                     v_cache);
+  return launch_status();
+}
+
+int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
+                              const pkv_bf16 *v_cache, const int32_t *block_tables,
+                              int32_t bt_stride, int64_t num_blocks, float scale,
+                              const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
+                              pkv_stream_t stream) {
+  int st = check_plan(plan, ws_bytes, ws);
+  if (st != PKV_OK) return st;
+  if (plan->num_items == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !out || bt_stride <= 0 || num_blocks <= 0)
+    return PKV_EINVAL;
+  const int G = plan->num_q_heads / plan->num_kv_heads;
+  AttnArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.bt = block_tables;
+  a.out = out;
+  char *w = static_cast<char *>(ws);
+  a.items = reinterpret_cast<const Item *>(w + plan->items_off);
+  a.part_ml = reinterpret_cast<float2 *>(w + plan->ml_off);
+  a.part_o = reinterpret_cast<float *>(w + plan->o_off);
+  a.num_blocks = num_blocks;
+  a.bt_stride = bt_stride;
+  a.num_items = plan->num_items;
+  a.Hq = plan->num_q_heads;
+  a.Hkv = plan->num_kv_heads;
+  a.log2G = pkv::log2_exact(G);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (a.log2G < 0) return PKV_EUNSUPPORTED;
+  if (plan->num_wide_items > 0)
+    hipLaunchKernelGGL(attention_kernel<true>, dim3(plan->num_items), dim3(64), 0,
+                       as_stream(stream), a);
+  else
+    hipLaunchKernelGGL(attention_kernel<false>, dim3(plan->num_items), dim3(64), 0,
+                       as_stream(stream), a);
+  return launch_status();
+}
+
+int pkv_split_kv_reduce(const pkv_plan_t *plan, const void *ws, size_t ws_bytes, pkv_bf16 *out,
+                        pkv_stream_t stream) {
+  int st = check_plan(plan, ws_bytes, ws);
+  if (st != PKV_OK) return st;
+  if (plan->num_merge == 0) return PKV_OK;
+  if (!out) return PKV_EINVAL;
+  const char *w = static_cast<const char *>(ws);
+  hipLaunchKernelGGL(merge_kernel, dim3(plan->num_merge), dim3(64), 0, as_stream(stream),
+                     reinterpret_cast<const Merge *>(w + plan->merge_off), plan->num_merge,
+                     reinterpret_cast<const float2 *>(w + plan->ml_off),
+                     reinterpret_cast<const float *>(w + plan->o_off), out);
+  return launch_status();
+}
+
+int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
+                               const pkv_bf16 *v_cache, const int32_t *block_tables,
+                               int32_t bt_stride, int64_t num_blocks, float scale,
+                               const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
+                               pkv_stream_t stream) {
+  int st = pkv_varlen_attention_main(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
+                                     scale, plan, ws, ws_bytes, out, stream);
+  if (st != PKV_OK) return st;
+  return pkv_split_kv_reduce(plan, ws, ws_bytes, out, stream);
+}
+
+int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                   pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q,
+                   const int32_t *seq_lens, const int32_t *block_tables, int32_t bt_stride,
+                   int64_t num_blocks, int64_t *slot_mapping, float scale,
+                   const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
+                   pkv_stream_t stream) {
+  if (!plan) return PKV_EINVAL;
+  int st = pkv_slot_mapping(cu_seqlens_q, seq_lens, block_tables, bt_stride, plan->num_seqs,
+                            plan->num_rows, num_blocks, slot_mapping, stream);
+  if (st != PKV_OK) return st;
+  st = pkv_paged_kv_append(k_new, v_new, slot_mapping, plan->num_rows, k_cache, v_cache,
+                           num_blocks, plan->num_kv_heads, plan->head_dim, stream);
+  if (st != PKV_OK) return st;
+  return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
+                                    scale, plan, ws, ws_bytes, out, stream);
+}
+
+}  // extern "C"

@@ -20,11 +20,14 @@ patterns stored as uint16):
   Tiles of blocks no table references are filled with a quiet-NaN pattern
   by default, so a reader that strays into them shows up at once.
 
-Values are N(0,1) draws rounded to bf16 (round to nearest even): uniform
-16-bit integers from ``numpy.random.Generator(PCG64(seed))`` index a table
-of the 65536 N(0,1) quantiles at (u + 0.5) / 65536, so every consumer sees
-the same bits.  Block placement is a seeded random permutation of the pool's
-block ids.  This module holds no attention arithmetic.
+Values are N(0,1) rounded to bf16 (nearest even), computed by the
+counter-based generator of ``synth.counter`` from (seed, tensor, element
+index), so every consumer sees the same bits and any block of a large pool
+can be computed on its own (``Pool``); the whole pool can be generated on
+the GPU from the same definition.  Lengths and block placement (a seeded
+random permutation of the pool's block ids) come from
+``numpy.random.Generator(PCG64(seed))``.  This module holds no attention
+arithmetic.
 """
 
 from __future__ import annotations
@@ -35,11 +38,13 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from . import counter
+
 BLOCK_SIZE = 16
 HEAD_DIM = 128
 NUM_Q_HEADS = 32
 NUM_KV_HEADS = 8
-QNAN_BF16 = np.uint16(0x7FC0)
+QNAN_BF16 = np.uint16(counter.QNAN_BF16)
 
 # seed of config i (1-based) is 149000 + i
 CONFIG_SEEDS = {i: 149000 + i for i in range(1, 6)}
@@ -54,31 +59,61 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-_NORMAL_TABLE = None
+# counter-generator stream ids of the batch tensors
+STREAM_Q, STREAM_K_NEW, STREAM_V_NEW, STREAM_K_POOL, STREAM_V_POOL = 1, 2, 3, 4, 5
 
 
-def _normal_table() -> np.ndarray:
-    """bf16 bits of the N(0,1) quantiles at (u + 0.5) / 65536, u = 0..65535:
-    indexing it with uniform 16-bit integers samples bf16(Z), Z ~ N(0,1),
-    truncated at about 4.3 sigma."""
-    global _NORMAL_TABLE
-    if _NORMAL_TABLE is None:
-        from scipy.special import ndtri
-        z = ndtri((np.arange(65536, dtype=np.float64) + 0.5) / 65536.0)
-        _NORMAL_TABLE = f32_to_bf16_bits(z.astype(np.float32))
-    return _NORMAL_TABLE
+class Pool:
+    """The pool's contents, [num_blocks, Hkv, 16*D] bf16 bits, computed on
+    demand: ``pool[blocks]`` gives the tiles of the listed blocks and
+    ``pool[b, h]`` one tile.  Element (b, h, e) is counter element
+    (b * Hkv + h) * 16D + e of this pool's stream; tiles of blocks no table
+    references hold ``unused_fill`` instead."""
 
+    def __init__(self, seed, stream, num_blocks, num_kv_heads, tile, referenced, unused_fill):
+        self.seed, self.stream = seed, stream
+        self.num_blocks, self.num_kv_heads, self.tile = num_blocks, num_kv_heads, tile
+        self.referenced = referenced
+        self.unused_fill = unused_fill
+        self.shape = (num_blocks, num_kv_heads, tile)
+        self.dtype = np.dtype(np.uint16)
 
-def bf16_normal(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0,1) draws as bf16 bits: uniform 16-bit integers from ``rng`` mapped
-    through the quantile table, in chunks so very large pools stay cheap."""
-    tab = _normal_table()
-    n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = tab[rng.integers(0, 65536, size=e - s, dtype=np.uint16)]
-    return out.reshape(shape)
+    def tiles(self, blocks) -> np.ndarray:
+        blocks = np.asarray(blocks, dtype=np.int64).reshape(-1)
+        per = self.num_kv_heads * self.tile
+        idx = blocks.astype(np.uint64)[:, None] * np.uint64(per) + np.arange(per, dtype=np.uint64)[None, :]
+        out = counter.normal_bf16_np(self.seed, self.stream, idx)
+        if self.unused_fill != "normal":
+            free = ~self.referenced[blocks]
+            out[free] = QNAN_BF16 if self.unused_fill == "nan" else 0
+        return out.reshape(blocks.shape[0], self.num_kv_heads, self.tile)
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            b, h = key
+            return self.tiles([int(b)])[0, h]
+        a = np.asarray(key)
+        if a.ndim == 0:
+            return self.tiles([int(a)])[0]
+        return self.tiles(a)
+
+    def materialize(self) -> np.ndarray:
+        return self.tiles(np.arange(self.num_blocks))
+
+    def copy(self) -> np.ndarray:
+        return self.materialize()
+
+    def to_device(self, device):
+        """int16 tensor [num_blocks, Hkv, tile] generated on ``device``."""
+        import torch
+        per = self.num_kv_heads * self.tile
+        t = counter.normal_bf16_range_torch(self.seed, self.stream, 0, self.num_blocks * per, device)
+        t = t.view(self.num_blocks, self.num_kv_heads, self.tile)
+        if self.unused_fill != "normal":
+            free = torch.from_numpy(np.nonzero(~self.referenced)[0]).to(device)
+            if free.numel():
+                t[free] = QNAN_BF16 if self.unused_fill == "nan" else 0
+        return t
 
 
 @dataclasses.dataclass
@@ -137,12 +172,13 @@ def make_batch(
     pool_factor: float = 1.25,
     shared_groups: Sequence[Tuple[Sequence[int], int]] = (),
     unused_fill: str = "nan",
-    pool: str = "draw",
+    pool: str = "lazy",
     rng: Optional[np.random.Generator] = None,
 ) -> Batch:
     """Draw one batch.
 
     ``seqs`` lists ``(cached, q_len)`` per sequence in packed order.
+    ``pool`` is "lazy" (a ``Pool``) or "materialize" (numpy arrays).
     ``shared_groups`` lists ``(members, n_blocks)``: the first ``n_blocks``
     logical blocks of every member point at the same physical blocks (a
     read-only shared prefix; each member must hold at least that many full
@@ -194,33 +230,22 @@ def make_batch(
     T = int(qlen.sum())
     cu = np.zeros(S + 1, dtype=np.int64)
     cu[1:] = np.cumsum(qlen)
-    q = bf16_normal(rng, (T, num_q_heads, head_dim))
-    k_new = bf16_normal(rng, (T, num_kv_heads, head_dim))
-    v_new = bf16_normal(rng, (T, num_kv_heads, head_dim))
+    q = counter.normal_bf16_range_np(seed, STREAM_Q, 0, T * num_q_heads * head_dim)
+    q = q.reshape(T, num_q_heads, head_dim)
+    k_new = counter.normal_bf16_range_np(seed, STREAM_K_NEW, 0, T * num_kv_heads * head_dim)
+    k_new = k_new.reshape(T, num_kv_heads, head_dim)
+    v_new = counter.normal_bf16_range_np(seed, STREAM_V_NEW, 0, T * num_kv_heads * head_dim)
+    v_new = v_new.reshape(T, num_kv_heads, head_dim)
 
     tile = BLOCK_SIZE * head_dim
-    if pool == "skip":
-        k_pool = v_pool = None
-    else:
-        k_pool = np.empty((num_blocks, num_kv_heads, tile), dtype=np.uint16)
-        v_pool = np.empty((num_blocks, num_kv_heads, tile), dtype=np.uint16)
-        referenced = np.zeros(num_blocks, dtype=bool)
-        referenced[bt[bt >= 0]] = True
-        ref_ids = np.nonzero(referenced)[0]
-        k_pool[ref_ids] = bf16_normal(rng, (ref_ids.size, num_kv_heads, tile))
-        v_pool[ref_ids] = bf16_normal(rng, (ref_ids.size, num_kv_heads, tile))
-        free_ids = np.nonzero(~referenced)[0]
-        if unused_fill == "nan":
-            k_pool[free_ids] = QNAN_BF16
-            v_pool[free_ids] = QNAN_BF16
-        elif unused_fill == "zero":
-            k_pool[free_ids] = 0
-            v_pool[free_ids] = 0
-        elif unused_fill == "normal":
-            k_pool[free_ids] = bf16_normal(rng, (free_ids.size, num_kv_heads, tile))
-            v_pool[free_ids] = bf16_normal(rng, (free_ids.size, num_kv_heads, tile))
-        else:
-            raise ValueError(unused_fill)
+    referenced = np.zeros(num_blocks, dtype=bool)
+    referenced[bt[bt >= 0]] = True
+    if unused_fill not in ("nan", "zero", "normal"):
+        raise ValueError(unused_fill)
+    k_pool = Pool(seed, STREAM_K_POOL, num_blocks, num_kv_heads, tile, referenced, unused_fill)
+    v_pool = Pool(seed, STREAM_V_POOL, num_blocks, num_kv_heads, tile, referenced, unused_fill)
+    if pool == "materialize":
+        k_pool, v_pool = k_pool.materialize(), v_pool.materialize()
 
     return Batch(
         name=name,
@@ -247,10 +272,11 @@ def permute_placement(batch: Batch, seed: int) -> Batch:
     ids and every block-table entry is renamed the same way."""
     rng = np.random.Generator(np.random.PCG64(seed))
     perm = rng.permutation(batch.num_blocks)
-    k_pool = np.empty_like(batch.k_pool)
-    v_pool = np.empty_like(batch.v_pool)
-    k_pool[perm] = batch.k_pool
-    v_pool[perm] = batch.v_pool
+    src_k, src_v = np.asarray(batch.k_pool.copy()), np.asarray(batch.v_pool.copy())
+    k_pool = np.empty_like(src_k)
+    v_pool = np.empty_like(src_v)
+    k_pool[perm] = src_k
+    v_pool[perm] = src_v
     bt = batch.block_tables.astype(np.int64)
     bt = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
     return dataclasses.replace(batch, k_pool=k_pool, v_pool=v_pool,

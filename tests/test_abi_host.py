@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every function the
+header declares, and its host-side planner partitions a ragged batch
+correctly (no GPU call is made here)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_149_amd as pkv
+from paged_kv_cache_149_amd import binding
+from synth import workloads as wl
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pkv.load_library()
+
+
+def test_library_exports_every_header_function(lib):
+    names = pkv.header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding._SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pkv_version() >= 100
+    assert lib.pkv_status_string(0) == b"ok"
+    assert lib.pkv_status_string(4) == b"workspace too small"
+
+
+def _plan(cu, sl, Hq=32, Hkv=8, D=128, bt=None, nb=0, **opts):
+    return pkv.pkv_plan(np.asarray(cu), np.asarray(sl), Hq, Hkv, D, block_tables=bt, num_blocks=nb,
+                        options=opts or None, host_only=True)
+
+
+def _coverage(plan, cu, sl, Hq, Hkv):
+    """Every (row, head) must be covered by items whose key ranges tile
+    [0, pos + 1) exactly once; merge entries must describe the splits."""
+    G = Hq // Hkv
+    items = plan.items()
+    cover = {}
+    for seq, kvh, t0, np_, pos0, k0, k1, part in items:
+        assert k0 % 32 == 0 and k1 > k0
+        assert cu[seq] <= t0 and t0 + np_ <= cu[seq + 1]
+        assert pos0 == sl[seq] - (cu[seq + 1] - cu[seq]) + (t0 - cu[seq])
+        assert k1 <= pos0 + np_
+        for pc in range(np_):
+            for ho in range(G):
+                cover.setdefault((t0 + pc, kvh * G + ho), []).append((k0, min(k1, pos0 + pc + 1), part, pc * G + ho))
+    T = cu[-1]
+    seq_of = np.searchsorted(cu, np.arange(T), side="right") - 1
+    merges = {int(m[0]): m for m in plan.merges()}
+    for t in range(T):
+        s = seq_of[t]
+        pos = sl[s] - (cu[s + 1] - cu[s]) + (t - cu[s])
+        for h in range(Hq):
+            rngs = sorted(cover[(t, h)])
+            keys = []
+            for k0, k1, _, _ in rngs:
+                keys.extend(range(k0, k1))
+            assert keys == list(range(pos + 1)), (t, h)
+            if len(rngs) > 1:
+                m = merges[t * Hq + h]
+                firsts = sorted(p + c for _, _, p, c in rngs)
+                assert m[2] == len(rngs) and m[1] == firsts[0]
+                assert firsts == [m[1] + k * m[3] for k in range(m[2])]
+            else:
+                assert rngs[0][2] == -1 and (t * Hq + h) not in merges
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 2), (32, 2), (16, 1)])
+def test_plan_covers_every_row_head_and_key(Hq, Hkv):
+    cu = np.array([0, 5, 6, 6, 7, 40, 41, 141])
+    sl = np.array([5, 8, 3, 4, 33, 1000, 150])
+    for opts in ({}, {"min_split_keys": 32, "target_items": 100000}, {"wide_tiles": 0}, {"wide_tiles": 1}):
+        plan = _plan(cu, sl, Hq, Hkv, **opts)
+        _coverage(plan, cu, sl, Hq, Hkv)
+
+
+def test_plan_orders_wide_then_longest_first():
+    b = wl.config_mixed_chunked(n_decode=64)
+    plan = _plan(b.cu_seqlens_q, b.seq_lens)
+    it = plan.items()
+    wide = it[:, 3] * 4 > 16
+    nw = plan.num_wide_items
+    assert nw > 0 and wide[:nw].all() and not wide[nw:].any()
+    lens = it[nw:, 6] - it[nw:, 5]
+    assert (np.diff(lens) <= 0).all()
+
+
+def test_plan_accounting_matches_visibility_counts():
+    cu, sl = [0, 5, 6, 7], [5, 8, 4]
+    plan = _plan(cu, sl)
+    grid = oracle.visibility_grid([0, 7, 3], [5, 1, 1])
+    assert plan.visible_pairs == int(grid.sum())
+    assert plan.kv_keys == sum(sl)
+    b = wl.config_worked_step()
+    assert _plan(b.cu_seqlens_q, b.seq_lens).num_items == 2 * 8 + 8  # R1 tile + 2 decode tiles, x8 heads
+
+
+def test_plan_splits_long_decode_contexts():
+    b = wl.config_long_shared()
+    plan = _plan(b.cu_seqlens_q, b.seq_lens)
+    assert plan.num_items >= 2048 and plan.num_merge == 16 * 32
+    _coverage(plan, b.cu_seqlens_q, b.seq_lens, 32, 8)
+
+
+@pytest.mark.parametrize("cu,sl,Hq,Hkv,D,code", [
+    ([1, 2], [3], 32, 8, 128, 1),          # cu[0] != 0
+    ([0, 3, 2], [3, 3], 32, 8, 128, 1),    # decreasing cu
+    ([0, 4], [3], 32, 8, 128, 1),          # q_len > seq_len
+    ([0, 1], [3], 32, 8, 64, 3),           # head_dim
+    ([0, 1], [3], 24, 8, 128, 3),          # G = 3
+    ([0, 1], [3], 64, 2, 128, 3),          # G = 32
+    ([0, 1], [3], 30, 8, 128, 3),          # Hq % Hkv
+])
+def test_plan_rejects_bad_metadata(cu, sl, Hq, Hkv, D, code):
+    with pytest.raises(pkv.PKVError) as e:
+        _plan(cu, sl, Hq, Hkv, D)
+    assert e.value.status == code
+
+
+def test_plan_validates_block_tables():
+    cu, sl = np.array([0, 1, 2]), np.array([17, 3])
+    bt = np.array([[3, 4], [5, -1]], dtype=np.int32)
+    _plan(cu, sl, bt=bt, nb=6)
+    bad = bt.copy()
+    bad[0, 1] = 6
+    with pytest.raises(pkv.PKVError) as e:
+        _plan(cu, sl, bt=bad, nb=6)
+    assert e.value.status == 2
+    with pytest.raises(pkv.PKVError):
+        _plan(cu, np.array([33, 3]), bt=bt, nb=6)   # needs 3 blocks, table has 2
+
+
+def test_workspace_size_query_and_too_small(lib):
+    cu = np.array([0, 1], dtype=np.int32)
+    sl = np.array([5000], dtype=np.int32)
+    st = binding.PlanStruct()
+    opts = binding.PlanOptions(0, 32, -1, 0)
+    args = [cu.ctypes.data_as(ctypes.c_void_p), sl.ctypes.data_as(ctypes.c_void_p), 1, 1, 32, 8, 128,
+            None, 0, 0, ctypes.byref(opts)]
+    assert lib.pkv_plan(*args, None, 0, None, 0, ctypes.byref(st), None) == 0
+    assert st.host_bytes > 0 and st.ws_bytes > st.host_bytes and st.num_merge == 32
+    buf = (ctypes.c_char * 16)()
+    assert lib.pkv_plan(*args, ctypes.cast(buf, ctypes.c_void_p), 16, None, 0, ctypes.byref(st), None) == 4

@@ -112,7 +112,7 @@ def test_gather_blockwise_equals_token_by_token():
 
 
 def test_append_round_trip_and_untouched_tiles():
-    b = small_batch([(37, 3), (15, 1), (0, 16)], D=16, unused_fill="normal")
+    b = small_batch([(37, 3), (15, 1), (0, 16)], D=16, unused_fill="normal", pool="materialize")
     slots = oracle.slot_mapping(b.cu_seqlens_q, b.seq_lens, b.block_tables)
     slots_skip = slots.copy()
     slots_skip[1] = -1
@@ -368,7 +368,7 @@ def test_single_visible_key_returns_its_value():
 
 
 def test_constant_values_give_the_constant():
-    b = small_batch([(33, 2), (7, 1)], D=16)
+    b = small_batch([(33, 2), (7, 1)], D=16, pool="materialize")
     c = wl.f32_to_bf16_bits(np.array([1.25, -0.5], dtype=np.float32))
     b.v_pool[:, 0, :] = c[0]
     b.v_pool[:, 1, :] = c[1]
