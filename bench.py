@@ -45,7 +45,22 @@ def parse():
     p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB fp32 copy kernel 5 times (HBM counter calibration)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise copy of known size: reads and writes 2^30 bytes
+    per launch, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}), flush=True)
 
 
 def log(msg):
@@ -54,6 +69,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this path has no "
               "multi-GPU form: the step shards by sequence with no exchange.", file=sys.stderr)

@@ -50,6 +50,10 @@ __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ inline u32x4 load16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Wave-uniform read-only load through the scalar data cache (s_load).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ inline int32_t sload(const int32_t *p, int64_t i) { return ((const_i32 *)p)[i]; }
+
 // fp32 -> bf16 (round to nearest even), packed two per dword; low half first
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;
@@ -138,6 +142,8 @@ struct AttnArgs {
 struct Chunk {
   u32x4 k[8];  // [m-tile][32-dim step]
   u32x4 v[8];  // [16-dim tile]
+  bool bad0;   // first block id out of range (wave-uniform)
+  bool bad1;   // second block needed and out of range (wave-uniform)
 };
 
 // Run one item with NT column tiles of 16 (NT = 1: up to 16 columns, NT = 4:
@@ -182,13 +188,12 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
     for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- block-table window: lane i holds entry (first block + base + i)
+  // ---- block ids are wave-uniform: scalar loads, fetched ahead of use
   const int32_t *btrow = a.bt + (int64_t)it.seq * a.bt_stride;
   const int kb0 = it.k0 >> 4;
-  // blocks of the item, never past the table row
-  const int nkb = min(((it.k1 + 15) >> 4), a.bt_stride) - kb0;
-  int bt_base = 0;
-  int btv = lane < nkb ? btrow[kb0 + lane] : -1;
+  // one past the last table entry the item may read (never past the row)
+  const int kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
+  auto block_id = [&](int lb) -> int { return lb < kb_end ? sload(btrow, lb) : -1; };
 
   const int nchunks = (it.k1 - it.k0 + 31) >> 5;
   const int64_t head_off = (int64_t)it.kvh * TILE;
@@ -201,37 +206,45 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
   const int v_sel = g >> 1;
   const int v_off = r * pkv::kBlock + 8 * (g & 1);         // + 16*dt*16
 
-  auto load_chunk = [&](int cc, Chunk &ch) {
-    const int rel0 = 2 * cc;
-    if (rel0 + 1 - bt_base >= 64) {  // slide the table window (uniform)
-      bt_base += 64;
-      btv = lane < nkb - bt_base ? btrow[kb0 + bt_base + lane] : -1;
-    }
+  // Chunk cc covers keys k0 + 32cc .. +31 in logical blocks kb0 + 2cc and
+  // kb0 + 2cc + 1.  When the second block is not needed it aliases the
+  // first (same cache lines): every key past k1 is masked out of the scores
+  // and its value zeroed, so its contents never matter.
+  auto load_chunk = [&](int cc, int b0, int b1, Chunk &ch) {
     const int key0 = it.k0 + 32 * cc;
-    const int b0 = __builtin_amdgcn_readlane(btv, rel0 - bt_base);
     const bool need1 = key0 + 16 < it.k1;
-    const int b1 = need1 ? __builtin_amdgcn_readlane(btv, rel0 + 1 - bt_base) : -1;
     const bool ok0 = b0 >= 0 && b0 < a.num_blocks;
     const bool ok1 = b1 >= 0 && b1 < a.num_blocks;
-    const int64_t t0 = ok0 ? (int64_t)b0 * blk_stride + head_off : 0;
-    const int64_t t1 = ok1 ? (int64_t)b1 * blk_stride + head_off : 0;
-    const bool kok = k_sel ? ok1 : ok0;
+    // addresses are always in bounds: an id outside [0, num_blocks) reads
+    // block 0 and is zeroed at compute time.  Every path issues the same 16
+    // loads, so the wait for this chunk can leave the next one in flight.
+    const int64_t t0 = (ok0 ? (int64_t)b0 * blk_stride : 0) + head_off;
+    const int64_t t1 = need1 && ok1 ? (int64_t)b1 * blk_stride + head_off : t0;
     const uint16_t *kp = a.kc + (k_sel ? t1 : t0) + k_row_off;
+    const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        ch.k[mt * 4 + c] = kok ? load16(kp + 4 * mt * D + 32 * c) : u32x4{0, 0, 0, 0};
-    const bool vok = v_sel ? ok1 : ok0;
-    const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off;
+      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16(kp + 4 * mt * D + 32 * c);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      ch.v[dt] = vok ? load16(vp + dt * 16 * pkv::kBlock) : u32x4{0, 0, 0, 0};
+    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16(vp + dt * 16 * pkv::kBlock);
+    ch.bad0 = !ok0;
+    ch.bad1 = need1 && !ok1;
   };
 
   auto compute_chunk = [&](int cc, Chunk &ch) {
     const int key0 = it.k0 + 32 * cc;
     const int kl = key0 + 8 * g;  // key of this lane's slot 0
+    if (ch.bad0 || ch.bad1) {
+      // table entry outside [0, num_blocks): that block's keys and values are 0
+      const bool kz = k_sel ? ch.bad1 : ch.bad0;
+      const bool vz = v_sel ? ch.bad1 : ch.bad0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (kz) ch.k[i] = u32x4{0, 0, 0, 0};
+        if (vz) ch.v[i] = u32x4{0, 0, 0, 0};
+      }
+    }
     if (key0 + 32 > it.k1) {
       // keys past the range may hold stale data: zero their V so 0 * garbage
       // cannot reach the accumulator
@@ -290,17 +303,31 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
       for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(ch.v[dt], pb[nt], acc[nt][dt]);
   };
 
-  // ---- main loop, one chunk of loads in flight ahead of the math
+  // ---- main loop: one chunk of K/V loads in flight ahead of the math,
+  // block ids two chunks ahead.  The loop body always issues both
+  // prefetches (the tail is peeled), so every wait leaves the next chunk's
+  // 16 loads outstanding.
   Chunk bufA, bufB;
-  load_chunk(0, bufA);
+  load_chunk(0, block_id(kb0), block_id(kb0 + 1), bufA);
+  int nb0 = block_id(kb0 + 2), nb1 = block_id(kb0 + 3);
   int cc = 0;
-  for (; cc + 2 <= nchunks; cc += 2) {
-    load_chunk(cc + 1, bufB);
+  for (; cc + 2 < nchunks; cc += 2) {
+    load_chunk(cc + 1, nb0, nb1, bufB);
+    nb0 = block_id(kb0 + 2 * cc + 4);
+    nb1 = block_id(kb0 + 2 * cc + 5);
     compute_chunk(cc, bufA);
-    if (cc + 2 < nchunks) load_chunk(cc + 2, bufA);
+    load_chunk(cc + 2, nb0, nb1, bufA);
+    nb0 = block_id(kb0 + 2 * cc + 6);
+    nb1 = block_id(kb0 + 2 * cc + 7);
     compute_chunk(cc + 1, bufB);
   }
-  if (cc < nchunks) compute_chunk(cc, bufA);
+  if (cc + 1 < nchunks) {
+    load_chunk(cc + 1, nb0, nb1, bufB);
+    compute_chunk(cc, bufA);
+    compute_chunk(cc + 1, bufB);
+  } else {
+    compute_chunk(cc, bufA);
+  }
 
   // ---- epilogue
 #pragma unroll
@@ -331,24 +358,35 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
 }
 
 template <bool kWide>
-__global__ __launch_bounds__(64) void attention_kernel(AttnArgs a) {
+__device__ __forceinline__ void attention_body(const AttnArgs &a) {
   const int idx = blockIdx.x;
   if (idx >= a.num_items) return;
   Item it;
   const int32_t *src = reinterpret_cast<const int32_t *>(a.items + idx);
-  it.seq = __builtin_amdgcn_readfirstlane(src[0]);
-  it.kvh = __builtin_amdgcn_readfirstlane(src[1]);
-  it.t0 = __builtin_amdgcn_readfirstlane(src[2]);
-  it.np = __builtin_amdgcn_readfirstlane(src[3]);
-  it.pos0 = __builtin_amdgcn_readfirstlane(src[4]);
-  it.k0 = __builtin_amdgcn_readfirstlane(src[5]);
-  it.k1 = __builtin_amdgcn_readfirstlane(src[6]);
-  it.part = __builtin_amdgcn_readfirstlane(src[7]);
+  it.seq = sload(src, 0);
+  it.kvh = sload(src, 1);
+  it.t0 = sload(src, 2);
+  it.np = sload(src, 3);
+  it.pos0 = sload(src, 4);
+  it.k0 = sload(src, 5);
+  it.k1 = sload(src, 6);
+  it.part = sload(src, 7);
   if (it.k1 <= it.k0 || it.np <= 0) return;
   if (kWide && (it.np << a.log2G) > pkv::kTileCols)
     run_item<4>(a, it);
   else
     run_item<1>(a, it);
+}
+
+// Narrow tiles only (decode rows and prefill tails): two waves per SIMD.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attention_kernel(AttnArgs a) {
+  attention_body<false>(a);
+}
+
+// Wide prefill tiles and narrow items in the same launch.
+__global__ __launch_bounds__(64) void attention_mixed_kernel(AttnArgs a) {
+  attention_body<true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -478,11 +516,10 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
   if (plan->num_wide_items > 0)
-    hipLaunchKernelGGL(attention_kernel<true>, dim3(plan->num_items), dim3(64), 0,
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_items), dim3(64), 0,
                        as_stream(stream), a);
   else
-    hipLaunchKernelGGL(attention_kernel<false>, dim3(plan->num_items), dim3(64), 0,
-                       as_stream(stream), a);
+    hipLaunchKernelGGL(attention_kernel, dim3(plan->num_items), dim3(64), 0, as_stream(stream), a);
   return launch_status();
 }
 
