@@ -3,9 +3,9 @@
 one MI355X.
 
 A step is the whole hot path on one synthetic batch resident in HBM: slot
-translation, KV append, the fused attention launch and the split merge
-(the same calls as pkv_paged_step, issued one by one so the attention
-launch can be bracketed with HIP events on its own stream).  The default
+translation + KV append (one launch), the fused attention launch and the
+split merge -- the calls pkv_paged_step makes, issued one by one so the
+attention launch can be bracketed with HIP events on its stream.  The default
 workload is the decode-only step: 64 sequences, one query row each,
 cached contexts uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128,
 bf16.
@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
+    p.add_argument("--narrow-waves", type=int, default=0, help="plan option (0 = library default)")
+    p.add_argument("--min-wave-keys", type=int, default=0, help="plan option (0 = library default)")
+    p.add_argument("--hbm-probe", action="store_true",
+                   help="only measure plain streaming read and copy rates with torch kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB fp32 copy kernel 5 times (HBM counter calibration)")
     return p.parse_args()
@@ -63,6 +67,28 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": 4 * n, "launches": 5}), flush=True)
 
 
+def hbm_probe():
+    """Reference rates of plain torch kernels on this GPU: a sum over 4 GiB
+    of bf16 (read-only) and an elementwise copy of 2 GiB."""
+    import torch
+    x = torch.ones(1 << 31, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(1 << 30, dtype=torch.bfloat16, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("sum_read_4GiB", lambda: x.sum(dtype=torch.float32), 2 << 30 << 1),
+                             ("copy_2GiB", lambda: y.copy_(x[: 1 << 30] * 1), 4 << 30)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 10
+        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps({"hbm_probe_GBs": res}), flush=True)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -71,6 +97,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.hbm_probe:
+        hbm_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); this path has no "
@@ -94,6 +123,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     plan = pkv.pkv_plan(batch.cu_seqlens_q, batch.seq_lens, batch.num_q_heads, batch.num_kv_heads,
                         batch.head_dim, block_tables=batch.block_tables, num_blocks=batch.num_blocks,
+                        options={"narrow_waves": args.narrow_waves, "min_wave_keys": args.min_wave_keys,
+                                 "wide_tiles": -1},
                         device=dev, stream=stream)
     slots = torch.empty(batch.num_rows, dtype=torch.int64, device=dev)
     out = torch.empty_like(t["q"])
@@ -103,9 +134,8 @@ def main():
           for _ in range(args.steps)]
 
     def step(i=None):
-        pkv.pkv_slot_mapping(t["cu_seqlens_q"], t["seq_lens"], t["block_tables"], t["num_blocks"],
-                             out=slots, stream=stream)
-        pkv.pkv_paged_kv_append(t["k_new"], t["v_new"], slots, t["k_cache"], t["v_cache"], stream=stream)
+        pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"], t["block_tables"],
+                            t["k_cache"], t["v_cache"], slot_mapping=slots, stream=stream)
         if i is not None:
             ev[i][0].record(stream)
         pkv.pkv_varlen_attention_main(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["scale"],
@@ -164,7 +194,8 @@ def main():
                    "q_heads": batch.num_q_heads, "kv_heads": batch.num_kv_heads,
                    "head_dim": batch.head_dim, "block_size": 16, "num_blocks": batch.num_blocks,
                    "kv_keys": int(plan.kv_keys), "items": int(plan.num_items),
-                   "split_keys": int(plan.split_keys)},
+                   "waves": int(plan.num_waves) + int(plan.num_wide_items),
+                   "wave_keys": int(plan.wave_keys)},
         "query_tok_s": round(batch.num_rows / (ms_step * 1e-3), 1),
         "kv_bytes_unique": nbytes["kv_unique"],
         "attention_flop": flop,

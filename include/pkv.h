@@ -114,15 +114,30 @@ int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
                         int32_t head_dim, pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Work partitioning (host).  Decode rows ("11.2 连续批处理与 PagedAttention",
- * section 11.2.2: attention runs per request inside one launch) become items
- * (sequence, kv head, key range); long contexts are split over the key axis
- * so the launch fills the chip, and split results are merged afterwards.
- * Rows of sequences with q_len > 1 (prefill and chunked prefill, whose
- * causal offset is the cached prefix: "Continuous Batching 深入实现", section
- * "一个 chunked prefill 请求怎么组织 attention") become tiles of query
- * positions x the kv head's query heads.  Wide tiles come first in the list,
- * then everything else longest-first.
+ * Slot translation and append in one launch: computes slot_mapping exactly
+ * as pkv_slot_mapping (and writes it: device int64[num_rows]) and copies
+ * each row's K/V into its slot exactly as pkv_paged_kv_append.  Errors as
+ * for pkv_slot_mapping; PKV_EUNSUPPORTED for head_dim != 128.
+ * ------------------------------------------------------------------------- */
+int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                    const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                    const int32_t *block_tables, int32_t bt_stride,
+                    int32_t num_seqs, int32_t num_rows, int64_t num_blocks,
+                    int64_t *slot_mapping, pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                    int32_t num_kv_heads, int32_t head_dim, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Work partitioning (host).  Rows of sequences with q_len > 1 (prefill and
+ * chunked prefill, whose causal offset is the cached prefix: "Continuous
+ * Batching 深入实现", section "一个 chunked prefill 请求怎么组织 attention")
+ * become tiles of query positions x the kv head's query heads; a wide tile
+ * (64 columns) is one wavefront's item.  Everything else -- decode rows and
+ * short tiles ("11.2 连续批处理与 PagedAttention", section 11.2.2: attention
+ * runs per request inside one launch) -- is a (tile, kv head) unit whose
+ * keys stream through the cache; all units' 32-key chunks are dealt out in
+ * equal contiguous shares to a fixed number of wavefronts, splitting a unit
+ * wherever a share ends, so every wavefront streams the same number of
+ * bytes however ragged the contexts are.  Split units are merged afterwards.
  *
  * The plan is written to h_staging (host memory; pinned memory lets the copy
  * run asynchronously) and, when ws is not NULL, copied to ws with
@@ -138,8 +153,8 @@ int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * plan->host_bytes then hold the sizes needed), PKV_EHIP.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_plan_options {
-  int32_t target_items;   /* aim for about this many items (0 = default) */
-  int32_t min_split_keys; /* shortest key split, multiple of 32 (0 = default) */
+  int32_t narrow_waves;   /* wavefronts sharing the decode work (0 = default) */
+  int32_t min_wave_keys;  /* smallest share per wavefront, keys (0 = default) */
   int32_t wide_tiles;     /* -1 auto, 0 never, 1 always use wide prefill tiles */
   int32_t reserved;
 } pkv_plan_options_t;
@@ -147,11 +162,13 @@ typedef struct pkv_plan_options {
 typedef struct pkv_plan {
   int32_t num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim;
   int32_t num_items;      /* attention work items */
-  int32_t num_wide_items; /* items with wide (64-column) tiles, at the front */
+  int32_t num_wide_items; /* wide tiles: items [0, num_wide_items), one per wavefront */
+  int32_t num_waves;      /* wavefronts walking the remaining items */
   int32_t num_merge;      /* merge entries (one per split output row x head) */
   int32_t num_part_cols;  /* partial-result columns in the workspace */
-  int32_t split_keys;     /* key-split length chosen for split items */
-  int64_t items_off, merge_off, ml_off, o_off; /* byte offsets into ws */
+  int32_t wave_keys;      /* keys per wavefront share */
+  int32_t reserved;
+  int64_t items_off, waves_off, merge_off, ml_off, o_off; /* byte offsets into ws */
   size_t ws_bytes;        /* workspace bytes this plan uses */
   size_t host_bytes;      /* host staging bytes this plan uses */
   int64_t kv_keys;        /* sum over sequences of visible keys (accounting) */
@@ -210,8 +227,8 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                                pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * The whole step on one stream: slot translation into slot_mapping (device
- * int64[T], written), append, attention, merge.  Attention reads the cache
+ * The whole step on one stream: pkv_slot_append (slot_mapping, device
+ * int64[T], is written), then pkv_paged_varlen_attention.  Attention reads the cache
  * after the append, so each row sees its own new key.
  * ------------------------------------------------------------------------- */
 int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     pkv_paged_step,
     pkv_paged_varlen_attention,
     pkv_plan,
+    pkv_slot_append,
     pkv_slot_mapping,
     pkv_split_kv_reduce,
     pkv_varlen_attention_main,

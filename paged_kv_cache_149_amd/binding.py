@@ -37,7 +37,7 @@ class PKVError(RuntimeError):
 
 
 class PlanOptions(ctypes.Structure):
-    _fields_ = [("target_items", ctypes.c_int32), ("min_split_keys", ctypes.c_int32),
+    _fields_ = [("narrow_waves", ctypes.c_int32), ("min_wave_keys", ctypes.c_int32),
                 ("wide_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
@@ -45,10 +45,11 @@ class PlanStruct(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_items", ctypes.c_int32),
-                ("num_wide_items", ctypes.c_int32), ("num_merge", ctypes.c_int32),
-                ("num_part_cols", ctypes.c_int32), ("split_keys", ctypes.c_int32),
-                ("items_off", ctypes.c_int64), ("merge_off", ctypes.c_int64),
-                ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
+                ("num_wide_items", ctypes.c_int32), ("num_waves", ctypes.c_int32),
+                ("num_merge", ctypes.c_int32), ("num_part_cols", ctypes.c_int32),
+                ("wave_keys", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("items_off", ctypes.c_int64), ("waves_off", ctypes.c_int64),
+                ("merge_off", ctypes.c_int64), ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
                 ("ws_bytes", ctypes.c_size_t), ("host_bytes", ctypes.c_size_t),
                 ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64)]
 
@@ -64,6 +65,8 @@ _SIGNATURES = {
     "pkv_version": (ctypes.c_int, []),
     "pkv_slot_mapping": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I64, _P, _P]),
     "pkv_paged_kv_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _P]),
+    "pkv_slot_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _P, _P, _P,
+                                       _I32, _I32, _P]),
     "pkv_plan": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _I64,
                                 ctypes.POINTER(PlanOptions), _P, _SZ, _P, _SZ,
                                 ctypes.POINTER(PlanStruct), _P]),
@@ -179,6 +182,29 @@ def pkv_paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=Non
         _stream(stream, dev)))
 
 
+def pkv_slot_append(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, k_cache, v_cache,
+                    slot_mapping=None, stream=None):
+    """Slot translation and append in one launch; returns slot_mapping."""
+    lib = load_library()
+    dev = k_cache.device
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, n, torch.bfloat16, dev)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seq_lens", seq_lens), ("block_tables", block_tables)):
+        _need(t, n, torch.int32, dev)
+    T, Hkv, D = k_new.shape
+    nb = k_cache.shape[0]
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(T, dtype=torch.int64, device=dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    _check("pkv_slot_append", lib.pkv_slot_append(
+        _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(block_tables),
+        block_tables.shape[1], seq_lens.shape[0], T, nb, _ptr(slot_mapping), _ptr(k_cache),
+        _ptr(v_cache), Hkv, D, _stream(stream, dev)))
+    return slot_mapping
+
+
 class Plan:
     """A work plan in a device workspace.  Keeps its pinned host staging
     buffer alive (and its copy event) as long as the plan lives."""
@@ -195,6 +221,13 @@ class Plan:
     def items(self) -> np.ndarray:
         n = self.st.num_items
         return self.staging[:n * ITEM_INTS * 4].numpy().view(np.int32).reshape(n, ITEM_INTS).copy()
+
+    def waves(self) -> np.ndarray:
+        """Item offsets of the narrow wavefronts (num_waves + 1 entries,
+        relative to item num_wide_items)."""
+        n = self.st.num_waves + 1
+        off = self.st.waves_off
+        return self.staging[off:off + n * 4].numpy().view(np.int32).copy()
 
     def merges(self) -> np.ndarray:
         n = self.st.num_merge

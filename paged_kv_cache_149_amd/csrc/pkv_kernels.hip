@@ -50,6 +50,12 @@ __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ inline u32x4 load16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Streaming load of cache data that is read once per launch: the
+// non-temporal hint keeps it from displacing reusable lines.
+__device__ inline u32x4 load16_stream(const uint16_t *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 // Wave-uniform read-only load through the scalar data cache (s_load).
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 __device__ inline int32_t sload(const int32_t *p, int64_t i) { return ((const_i32 *)p)[i]; }
@@ -66,13 +72,12 @@ __device__ inline float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v
 // ---------------------------------------------------------------------------
 // slot translation
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void slot_mapping_kernel(
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T,
-    int64_t num_blocks, int64_t *__restrict__ slots) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  // last s with cu[s] <= t (cu[S] = T > t)
+// Slot of packed row t: find its sequence s (last s with cu[s] <= t; cu[S] =
+// T > t), its position seq_lens[s] - q_len_s + (t - cu[s]), then
+// block_table[s][pos / 16] * 16 + pos % 16.  -1 if the entry is unusable.
+__device__ inline int64_t row_slot(const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
+                                   const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int t,
+                                   int64_t num_blocks) {
   int lo = 0, hi = S;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -81,30 +86,27 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   const int s = lo < S ? lo : S - 1;
   const int ql = cu[s + 1] - cu[s];
   const int pos = seq_lens[s] - ql + (t - cu[s]);
-  int64_t slot = -1;
-  if (pos >= 0 && (pos >> 4) < bt_stride) {
-    const int b = bt[(int64_t)s * bt_stride + (pos >> 4)];
-    if (b >= 0 && b < num_blocks) slot = (int64_t)b * pkv::kBlock + (pos & 15);
-  }
-  slots[t] = slot;
+  if (pos < 0 || (pos >> 4) >= bt_stride) return -1;
+  const int b = bt[(int64_t)s * bt_stride + (pos >> 4)];
+  if (b < 0 || b >= num_blocks) return -1;
+  return (int64_t)b * pkv::kBlock + (pos & 15);
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T,
+    int64_t num_blocks, int64_t *__restrict__ slots) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  slots[t] = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
 }
 
 // ---------------------------------------------------------------------------
 // append: one thread per (row, kv head, 8 dimensions)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kv_append_kernel(
-    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-    const int64_t *__restrict__ slots, int32_t T, int32_t Hkv, int64_t num_blocks,
-    uint16_t *__restrict__ kc, uint16_t *__restrict__ vc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)Hkv * (D / 8);
-  if (idx >= (int64_t)T * per_row) return;
-  const int t = (int)(idx / per_row);
-  const int rem = (int)(idx - (int64_t)t * per_row);
-  const int h = rem / (D / 8);
-  const int d0 = (rem % (D / 8)) * 8;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_blocks * pkv::kBlock) return;
+__device__ inline void append_one(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+                                  int t, int h, int d0, int Hkv, int64_t slot, uint16_t *__restrict__ kc,
+                                  uint16_t *__restrict__ vc) {
   const int64_t b = slot >> 4;
   const int o = (int)(slot & 15);
   const int64_t src = ((int64_t)t * Hkv + h) * D + d0;
@@ -118,6 +120,38 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
 }
 
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    const int64_t *__restrict__ slots, int32_t T, int32_t Hkv, int64_t num_blocks,
+    uint16_t *__restrict__ kc, uint16_t *__restrict__ vc) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)Hkv * (D / 8);
+  if (idx >= (int64_t)T * per_row) return;
+  const int t = (int)(idx / per_row);
+  const int rem = (int)(idx - (int64_t)t * per_row);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * pkv::kBlock) return;
+  append_one(k_new, v_new, t, rem / (D / 8), (rem % (D / 8)) * 8, Hkv, slot, kc, vc);
+}
+
+// slot translation and append in one launch (the whole-step entry point)
+__global__ __launch_bounds__(256) void slot_append_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
+    int64_t num_blocks, int64_t *__restrict__ slots, uint16_t *__restrict__ kc,
+    uint16_t *__restrict__ vc) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = (int64_t)Hkv * (D / 8);
+  if (idx >= (int64_t)T * per_row) return;
+  const int t = (int)(idx / per_row);
+  const int rem = (int)(idx - (int64_t)t * per_row);
+  const int64_t slot = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
+  if (rem == 0) slots[t] = slot;
+  if (slot < 0) return;
+  append_one(k_new, v_new, t, rem / (D / 8), (rem % (D / 8)) * 8, Hkv, slot, kc, vc);
+}
+
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
@@ -128,11 +162,14 @@ struct AttnArgs {
   const int32_t *bt;
   uint16_t *out;
   const Item *items;
+  const int32_t *waves;  // item offsets of the narrow wavefronts (after the wide items)
   float2 *part_ml;
   float *part_o;
   int64_t num_blocks;
   int32_t bt_stride;
   int32_t num_items;
+  int32_t num_wide;
+  int32_t num_waves;
   int32_t Hq;
   int32_t Hkv;
   int32_t log2G;
@@ -225,9 +262,9 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16(kp + 4 * mt * D + 32 * c);
+      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * D + 32 * c);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16(vp + dt * 16 * pkv::kBlock);
+    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * pkv::kBlock);
     ch.bad0 = !ok0;
     ch.bad1 = need1 && !ok1;
   };
@@ -357,10 +394,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
   }
 }
 
-template <bool kWide>
-__device__ __forceinline__ void attention_body(const AttnArgs &a) {
-  const int idx = blockIdx.x;
-  if (idx >= a.num_items) return;
+__device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
   Item it;
   const int32_t *src = reinterpret_cast<const int32_t *>(a.items + idx);
   it.seq = sload(src, 0);
@@ -371,11 +405,32 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
   it.k0 = sload(src, 5);
   it.k1 = sload(src, 6);
   it.part = sload(src, 7);
-  if (it.k1 <= it.k0 || it.np <= 0) return;
-  if (kWide && (it.np << a.log2G) > pkv::kTileCols)
-    run_item<4>(a, it);
-  else
-    run_item<1>(a, it);
+  return it;
+}
+
+// Workgroup b < num_wide runs wide item b; workgroup num_wide + w walks the
+// items of narrow wavefront w in order.
+template <bool kWide>
+__device__ __forceinline__ void attention_body(const AttnArgs &a) {
+  const int b = blockIdx.x;
+  if (kWide && b < a.num_wide) {
+    const Item it = load_item(a, b);
+    if (it.k1 > it.k0 && it.np > 0) {
+      if ((it.np << a.log2G) > pkv::kTileCols)
+        run_item<4>(a, it);
+      else
+        run_item<1>(a, it);
+    }
+    return;
+  }
+  const int w = b - (kWide ? a.num_wide : 0);
+  if (w >= a.num_waves) return;
+  const int i0 = a.num_wide + sload(a.waves, w);
+  const int i1 = a.num_wide + sload(a.waves, w + 1);
+  for (int i = i0; i < i1; ++i) {
+    const Item it = load_item(a, i);
+    if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
+  }
 }
 
 // Narrow tiles only (decode rows and prefill tails): two waves per SIMD.
@@ -505,21 +560,24 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.out = out;
   char *w = static_cast<char *>(ws);
   a.items = reinterpret_cast<const Item *>(w + plan->items_off);
+  a.waves = reinterpret_cast<const int32_t *>(w + plan->waves_off);
   a.part_ml = reinterpret_cast<float2 *>(w + plan->ml_off);
   a.part_o = reinterpret_cast<float *>(w + plan->o_off);
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
   a.num_items = plan->num_items;
+  a.num_wide = plan->num_wide_items;
+  a.num_waves = plan->num_waves;
   a.Hq = plan->num_q_heads;
   a.Hkv = plan->num_kv_heads;
   a.log2G = pkv::log2_exact(G);
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
   if (plan->num_wide_items > 0)
-    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_items), dim3(64), 0,
-                       as_stream(stream), a);
-  else
-    hipLaunchKernelGGL(attention_kernel, dim3(plan->num_items), dim3(64), 0, as_stream(stream), a);
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_wide_items + plan->num_waves), dim3(64),
+                       0, as_stream(stream), a);
+  else if (plan->num_waves > 0)
+    hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();
 }
 
@@ -548,6 +606,27 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   return pkv_split_kv_reduce(plan, ws, ws_bytes, out, stream);
 }
 
+int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t *cu_seqlens_q,
+                    const int32_t *seq_lens, const int32_t *block_tables, int32_t bt_stride,
+                    int32_t num_seqs, int32_t num_rows, int64_t num_blocks, int64_t *slot_mapping,
+                    pkv_bf16 *k_cache, pkv_bf16 *v_cache, int32_t num_kv_heads, int32_t head_dim,
+                    pkv_stream_t stream) {
+  if (num_seqs < 0 || num_rows < 0 || bt_stride < 0 || num_blocks < 0 || num_kv_heads <= 0)
+    return PKV_EINVAL;
+  if (head_dim != D) return PKV_EUNSUPPORTED;
+  if (num_rows == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables ||
+      !slot_mapping || num_seqs == 0)
+    return PKV_EINVAL;
+  const int64_t total = (int64_t)num_rows * num_kv_heads * (D / 8);
+  const int64_t grid = (total + 255) / 256;
+  if (grid > INT32_MAX) return PKV_ERANGE;
+  hipLaunchKernelGGL(slot_append_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
+                     k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs,
+                     num_rows, num_kv_heads, num_blocks, slot_mapping, k_cache, v_cache);
+  return launch_status();
+}
+
 int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_new,
                    pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q,
                    const int32_t *seq_lens, const int32_t *block_tables, int32_t bt_stride,
@@ -555,11 +634,9 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
                    const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream) {
   if (!plan) return PKV_EINVAL;
-  int st = pkv_slot_mapping(cu_seqlens_q, seq_lens, block_tables, bt_stride, plan->num_seqs,
-                            plan->num_rows, num_blocks, slot_mapping, stream);
-  if (st != PKV_OK) return st;
-  st = pkv_paged_kv_append(k_new, v_new, slot_mapping, plan->num_rows, k_cache, v_cache,
-                           num_blocks, plan->num_kv_heads, plan->head_dim, stream);
+  const int st = pkv_slot_append(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride,
+                                 plan->num_seqs, plan->num_rows, num_blocks, slot_mapping, k_cache,
+                                 v_cache, plan->num_kv_heads, plan->head_dim, stream);
   if (st != PKV_OK) return st;
   return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
                                     scale, plan, ws, ws_bytes, out, stream);

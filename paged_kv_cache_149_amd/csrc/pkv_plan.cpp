@@ -1,17 +1,19 @@
 // Host-side work partitioning for the fused varlen paged-attention launch.
 //
-// A step's sequences fall into two kinds ("11.2 连续批处理与 PagedAttention",
+// A step's rows fall into two kinds ("11.2 连续批处理与 PagedAttention",
 // section 11.2.2: prefill rows and decode rows share one packed step):
-//  * q_len == 1 (decode) and short q_len tiles: one item per (tile, kv head,
-//    key split).  Long contexts are split over the key axis so that the
-//    launch has enough items to fill 256 CUs even when the step holds few
-//    sequences; the splits are merged afterwards.
 //  * q_len > 1 (prefill / chunked prefill, causal offset = cached prefix:
 //    "Continuous Batching 深入实现", section "一个 chunked prefill 请求怎么组织
-//    attention"): tiles of query positions x the kv head's query heads; a wide
-//    tile holds 64 columns (64 / G positions), a narrow one 16.
-// Items are ordered wide first, then by decreasing key count, so the longest
-// work starts first and short items fill the tail.
+//    attention"): tiles of query positions x the kv head's query heads.  A
+//    wide tile (64 columns) is one wavefront's whole item, placed first.
+//  * Decode rows and the short tails of prefill rows: narrow (<= 16 column)
+//    units (tile, kv head), each a stream of 32-key chunks.  All chunks of all
+//    units are dealt out in equal contiguous shares to a fixed number of
+//    wavefronts ("stream-K" style): wavefront w takes chunks
+//    [w*C/W, (w+1)*C/W) of the concatenated units, so a long context is cut
+//    across several wavefronts and several short ones share one, and every
+//    wavefront streams the same number of bytes.  A unit cut into several
+//    segments writes partial results that a merge launch combines.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -25,8 +27,8 @@ namespace {
 using pkv::Item;
 using pkv::Merge;
 
-constexpr int kDefaultTargetItems = 8192;
-constexpr int kDefaultMinSplit = 256;
+constexpr int kDefaultNarrowWaves = 1024;   // 4 wavefronts per CU on 256 CUs
+constexpr int kDefaultMinWaveKeys = 512;
 
 int round_up32(int64_t x) { return (int)((x + 31) / 32 * 32); }
 
@@ -69,17 +71,16 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     }
   }
 
-  const int target = (opts && opts->target_items > 0) ? opts->target_items : kDefaultTargetItems;
-  int min_split = (opts && opts->min_split_keys > 0) ? opts->min_split_keys : kDefaultMinSplit;
-  min_split = round_up32(std::max(32, min_split));
+  const int want_waves = (opts && opts->narrow_waves > 0) ? opts->narrow_waves : kDefaultNarrowWaves;
+  const int min_wave_keys = (opts && opts->min_wave_keys > 0) ? opts->min_wave_keys : kDefaultMinWaveKeys;
   const int wide_opt = opts ? opts->wide_tiles : -1;
   const int narrow_pos = pkv::kTileCols / G;  // positions per narrow tile
   const int wide_pos = pkv::kWideCols / G;    // positions per wide tile
 
-  // ---- tiles: (seq, t0, np, pos0, keys) per kv head
+  // ---- tiles: (seq, t0, np, pos0, keys)
   struct Tile { int32_t seq, t0, np, pos0, keys; bool wide; };
-  std::vector<Tile> tiles;
-  int64_t narrow_keys = 0, kv_keys = 0, pairs = 0;
+  std::vector<Tile> wide_tiles, narrow_tiles;
+  int64_t kv_keys = 0, pairs = 0;
   bool any_prefill = false;
   for (int s = 0; s < num_seqs; ++s) if (h_cu[s + 1] - h_cu[s] > 1) any_prefill = true;
   const bool use_wide = wide_opt == 1 || (wide_opt < 0 && any_prefill);
@@ -95,48 +96,88 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
       const bool wide = use_wide && left > narrow_pos;
       const int np = std::min(left, wide ? wide_pos : narrow_pos);
       Tile t{s, h_cu[s] + j, np, c + j, c + j + np, wide};
-      if (!wide) narrow_keys += t.keys;
-      tiles.push_back(t);
+      (wide ? wide_tiles : narrow_tiles).push_back(t);
       j += np;
     }
   }
-  // key-split length for narrow tiles
-  int split = round_up32((narrow_keys * Hkv + target - 1) / std::max(1, target));
-  split = std::max(split, min_split);
 
   std::vector<Item> items;
   std::vector<Merge> merges;
+  std::vector<int32_t> wave_off;
   int64_t part_cols = 0;
-  int n_wide = 0;
-  for (const Tile &t : tiles) {
+
+  // wide tiles: one item each, longest first
+  std::stable_sort(wide_tiles.begin(), wide_tiles.end(),
+                   [](const Tile &x, const Tile &y) { return x.keys > y.keys; });
+  for (const Tile &t : wide_tiles)
+    for (int h = 0; h < Hkv; ++h) items.push_back(Item{t.seq, h, t.t0, t.np, t.pos0, 0, t.keys, -1});
+  const int n_wide = (int)items.size();
+
+  // narrow units (tile, kv head) in order; chunk counts
+  const int64_t n_units = (int64_t)narrow_tiles.size() * Hkv;
+  int64_t total_chunks = 0;
+  for (const Tile &t : narrow_tiles) total_chunks += (int64_t)Hkv * ((t.keys + 31) / 32);
+  int W = 0;
+  int wave_keys = 0;
+  if (total_chunks > 0) {
+    const int64_t by_size = (total_chunks * 32 + min_wave_keys - 1) / min_wave_keys;
+    W = (int)std::max<int64_t>(1, std::min<int64_t>(want_waves, by_size));
+    wave_keys = (int)((total_chunks + W - 1) / W * 32);
+  }
+  auto unit_tile = [&](int64_t u) -> const Tile & { return narrow_tiles[u / Hkv]; };
+  auto unit_chunks = [&](int64_t u) -> int { return (unit_tile(u).keys + 31) / 32; };
+  // pass 1: segments per unit (chunk boundaries of the wave shares)
+  std::vector<int32_t> nseg(n_units, 0);
+  {
+    int64_t u = 0, done = 0;  // chunks of unit u already dealt
+    for (int w = 0; w < W; ++w) {
+      int64_t room = total_chunks / W + (w < total_chunks % W ? 1 : 0);
+      while (room > 0 && u < n_units) {
+        const int64_t take = std::min<int64_t>(room, unit_chunks(u) - done);
+        ++nseg[u];
+        done += take;
+        room -= take;
+        if (done == unit_chunks(u)) { ++u; done = 0; }
+      }
+    }
+  }
+  // partial columns and merge entries for cut units
+  std::vector<int64_t> part_base(n_units, -1);
+  for (int64_t u = 0; u < n_units; ++u) {
+    if (nseg[u] <= 1) continue;
+    const Tile &t = unit_tile(u);
+    const int h = (int)(u % Hkv);
     const int ncols = t.np * G;
-    const int nsplit = t.wide ? 1 : (int)((t.keys + split - 1) / split);
-    for (int h = 0; h < Hkv; ++h) {
-      int64_t base = -1;
-      if (nsplit > 1) {
-        base = part_cols;
-        part_cols += (int64_t)nsplit * ncols;
-        for (int col = 0; col < ncols; ++col) {
-          const int pc = col >> log2G, ho = col & (G - 1);
-          merges.push_back(Merge{(t.t0 + pc) * Hq + h * G + ho, (int32_t)(base + col), nsplit, ncols});
-        }
+    part_base[u] = part_cols;
+    part_cols += (int64_t)nseg[u] * ncols;
+    for (int col = 0; col < ncols; ++col) {
+      const int pc = col >> log2G, ho = col & (G - 1);
+      merges.push_back(Merge{(t.t0 + pc) * Hq + h * G + ho, (int32_t)(part_base[u] + col), nseg[u], ncols});
+    }
+  }
+  // pass 2: emit each wave's segments as items, in wave order
+  {
+    int64_t u = 0, done = 0;
+    int seg = 0;
+    wave_off.push_back(0);
+    for (int w = 0; w < W; ++w) {
+      int64_t room = total_chunks / W + (w < total_chunks % W ? 1 : 0);
+      while (room > 0 && u < n_units) {
+        const Tile &t = unit_tile(u);
+        const int64_t take = std::min<int64_t>(room, unit_chunks(u) - done);
+        const int k0 = (int)(done * 32);
+        const int k1 = (int)std::min<int64_t>(t.keys, (done + take) * 32);
+        const int32_t part = part_base[u] < 0 ? -1 : (int32_t)(part_base[u] + (int64_t)seg * t.np * G);
+        items.push_back(Item{t.seq, (int32_t)(u % Hkv), t.t0, t.np, t.pos0, k0, k1, part});
+        ++seg;
+        done += take;
+        room -= take;
+        if (done == unit_chunks(u)) { ++u; done = 0; seg = 0; }
       }
-      for (int k = 0; k < nsplit; ++k) {
-        const int k0 = k * split;
-        const int k1 = k + 1 == nsplit ? t.keys : k0 + split;
-        items.push_back(Item{t.seq, h, t.t0, t.np, t.pos0, k0, k1,
-                             nsplit > 1 ? (int32_t)(base + (int64_t)k * ncols) : -1});
-      }
-      if (t.wide) ++n_wide;
+      wave_off.push_back((int32_t)(items.size() - n_wide));
     }
   }
   if (part_cols > INT32_MAX || (int64_t)items.size() > INT32_MAX / 2) return PKV_ERANGE;
-  // wide items first, then longest first (stable: equal lengths keep order)
-  std::stable_sort(items.begin(), items.end(), [&](const Item &a, const Item &b) {
-    const bool wa = a.np * G > pkv::kTileCols, wb = b.np * G > pkv::kTileCols;
-    if (wa != wb) return wa;
-    return (a.k1 - a.k0) > (b.k1 - b.k0);
-  });
 
   // ---- sizes
   plan->num_seqs = num_seqs;
@@ -146,26 +187,30 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   plan->head_dim = head_dim;
   plan->num_items = (int32_t)items.size();
   plan->num_wide_items = n_wide;
+  plan->num_waves = W;
   plan->num_merge = (int32_t)merges.size();
   plan->num_part_cols = (int32_t)part_cols;
-  plan->split_keys = split;
+  plan->wave_keys = wave_keys;
   plan->kv_keys = kv_keys;
   plan->visible_pairs = pairs;
   const size_t items_b = pkv::align_up(items.size() * sizeof(Item));
+  const size_t waves_b = pkv::align_up(wave_off.size() * sizeof(int32_t));
   const size_t merge_b = pkv::align_up(merges.size() * sizeof(Merge));
   plan->items_off = 0;
-  plan->merge_off = (int64_t)items_b;
-  plan->ml_off = (int64_t)(items_b + merge_b);
+  plan->waves_off = (int64_t)items_b;
+  plan->merge_off = (int64_t)(items_b + waves_b);
+  plan->ml_off = (int64_t)(items_b + waves_b + merge_b);
   plan->o_off = plan->ml_off + (int64_t)pkv::align_up((size_t)part_cols * 8);
   plan->ws_bytes = (size_t)plan->o_off + (size_t)part_cols * pkv::kHeadDim * 4;
-  plan->host_bytes = items_b + merge_b;
+  plan->host_bytes = items_b + waves_b + merge_b;
   if (!h_staging) return PKV_OK;  // size query
   if (h_staging_bytes < plan->host_bytes) return PKV_EWORKSPACE;
   if (ws && ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
 
   char *hs = static_cast<char *>(h_staging);
   if (!items.empty()) std::memcpy(hs, items.data(), items.size() * sizeof(Item));
-  if (!merges.empty()) std::memcpy(hs + items_b, merges.data(), merges.size() * sizeof(Merge));
+  if (!wave_off.empty()) std::memcpy(hs + items_b, wave_off.data(), wave_off.size() * sizeof(int32_t));
+  if (!merges.empty()) std::memcpy(hs + items_b + waves_b, merges.data(), merges.size() * sizeof(Merge));
   if (ws && plan->host_bytes > 0) {
     hipError_t e = hipMemcpyAsync(ws, h_staging, plan->host_bytes, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));

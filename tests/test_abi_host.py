@@ -76,20 +76,46 @@ def _coverage(plan, cu, sl, Hq, Hkv):
 def test_plan_covers_every_row_head_and_key(Hq, Hkv):
     cu = np.array([0, 5, 6, 6, 7, 40, 41, 141])
     sl = np.array([5, 8, 3, 4, 33, 1000, 150])
-    for opts in ({}, {"min_split_keys": 32, "target_items": 100000}, {"wide_tiles": 0}, {"wide_tiles": 1}):
+    for opts in ({}, {"min_wave_keys": 32, "narrow_waves": 100000}, {"narrow_waves": 3},
+                 {"wide_tiles": 0}, {"wide_tiles": 1}):
         plan = _plan(cu, sl, Hq, Hkv, **opts)
         _coverage(plan, cu, sl, Hq, Hkv)
 
 
-def test_plan_orders_wide_then_longest_first():
-    b = wl.config_mixed_chunked(n_decode=64)
+def test_plan_wide_items_first_then_balanced_waves():
+    b = wl.config_mixed_chunked(n_decode=64, pool="lazy")
     plan = _plan(b.cu_seqlens_q, b.seq_lens)
     it = plan.items()
     wide = it[:, 3] * 4 > 16
     nw = plan.num_wide_items
     assert nw > 0 and wide[:nw].all() and not wide[nw:].any()
-    lens = it[nw:, 6] - it[nw:, 5]
+    lens = it[:nw, 6] - it[:nw, 5]
     assert (np.diff(lens) <= 0).all()
+    _check_waves(plan)
+
+
+def _check_waves(plan):
+    """Wave shares tile the narrow items in order, and every wave streams
+    the same number of 32-key chunks (to within one)."""
+    it = plan.items()
+    off = plan.waves()
+    nw = plan.num_wide_items
+    assert off[0] == 0 and off[-1] == plan.num_items - nw and (np.diff(off) >= 1).all()
+    chunks = []
+    for w in range(plan.num_waves):
+        seg = it[nw + off[w]:nw + off[w + 1]]
+        chunks.append(int(((seg[:, 6] - seg[:, 5] + 31) // 32).sum()))
+    assert max(chunks) - min(chunks) <= 1, (min(chunks), max(chunks))
+    assert max(chunks) * 32 <= plan.wave_keys
+
+
+@pytest.mark.parametrize("waves", [1, 7, 1024, 5000])
+def test_plan_balances_ragged_decode(waves):
+    b = wl.config_decode64(pool="lazy")
+    plan = _plan(b.cu_seqlens_q, b.seq_lens, narrow_waves=waves, min_wave_keys=32)
+    assert plan.num_waves == min(waves, int(((b.seq_lens + 31) // 32).sum()) * 8)
+    _check_waves(plan)
+    _coverage(plan, b.cu_seqlens_q, b.seq_lens, 32, 8)
 
 
 def test_plan_accounting_matches_visibility_counts():
@@ -99,14 +125,16 @@ def test_plan_accounting_matches_visibility_counts():
     assert plan.visible_pairs == int(grid.sum())
     assert plan.kv_keys == sum(sl)
     b = wl.config_worked_step()
-    assert _plan(b.cu_seqlens_q, b.seq_lens).num_items == 2 * 8 + 8  # R1 tile + 2 decode tiles, x8 heads
+    p = _plan(b.cu_seqlens_q, b.seq_lens)
+    assert p.num_wide_items == 8 and p.num_items == 8 + 16   # R1's tile and 2 decode units, x8 heads
 
 
 def test_plan_splits_long_decode_contexts():
     b = wl.config_long_shared()
     plan = _plan(b.cu_seqlens_q, b.seq_lens)
-    assert plan.num_items >= 2048 and plan.num_merge == 16 * 32
+    assert plan.num_waves == 1024 and plan.num_merge == 16 * 32
     _coverage(plan, b.cu_seqlens_q, b.seq_lens, 32, 8)
+    _check_waves(plan)
 
 
 @pytest.mark.parametrize("cu,sl,Hq,Hkv,D,code", [
@@ -141,7 +169,7 @@ def test_workspace_size_query_and_too_small(lib):
     cu = np.array([0, 1], dtype=np.int32)
     sl = np.array([5000], dtype=np.int32)
     st = binding.PlanStruct()
-    opts = binding.PlanOptions(0, 32, -1, 0)
+    opts = binding.PlanOptions(1024, 32, -1, 0)
     args = [cu.ctypes.data_as(ctypes.c_void_p), sl.ctypes.data_as(ctypes.c_void_p), 1, 1, 32, 8, 128,
             None, 0, 0, ctypes.byref(opts)]
     assert lib.pkv_plan(*args, None, 0, None, 0, ctypes.byref(st), None) == 0

@@ -198,8 +198,8 @@ def test_gqa_ratios(dev, Hq, Hkv):
 
 
 @pytest.mark.parametrize("opts", [
-    {"min_split_keys": 32, "target_items": 1 << 20},   # every context split into 32-key pieces
-    {"min_split_keys": 64, "target_items": 1 << 20, "wide_tiles": 0},
+    {"min_wave_keys": 32, "narrow_waves": 1 << 20},   # one 32-key chunk per wavefront
+    {"min_wave_keys": 64, "narrow_waves": 3, "wide_tiles": 0},  # three wavefronts walk everything
     {"wide_tiles": 1},
 ])
 def test_plan_options_same_result(dev, opts):
@@ -228,7 +228,7 @@ def test_attention_entry_points_agree(dev):
     b = wl.config_decode64()
     t = to_device(b, dev)
     plan = pkv.pkv_plan(b.cu_seqlens_q, b.seq_lens, 32, 8, 128, block_tables=b.block_tables,
-                        num_blocks=b.num_blocks, options={"min_split_keys": 64, "target_items": 1 << 16},
+                        num_blocks=b.num_blocks, options={"min_wave_keys": 64, "narrow_waves": 1 << 16},
                         device=dev)
     assert plan.num_merge > 0
     slots = pkv.pkv_slot_mapping(t["cu_seqlens_q"], t["seq_lens"], t["block_tables"], b.num_blocks)
