@@ -25,6 +25,8 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_149_amd", "csrc", "pkv_kernels.hip")
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "packed-step attention: KV GB/s + query tok/s vs HBM/MFMA roofline, 1 GPU"
@@ -87,6 +89,27 @@ def hbm_probe():
         ms = a.elapsed_time(b) / 10
         res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     print(json.dumps({"hbm_probe_GBs": res}), flush=True)
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 --pmc
+    record for this workload (FETCH_SIZE and WRITE_SIZE, each scaled by the
+    factor a plain copy kernel of known size gives), or None when there is
+    no record or the kernel source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def log(msg):
@@ -170,7 +193,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": None, "kernel": "attention_kernel", "avg_ms": round(attn_ms, 5),
+    roof.update({"traffic": measured_traffic(args.workload), "kernel": "attention_kernel", "avg_ms": round(attn_ms, 5),
                  "bytes_per_launch": nbytes["total"], "flop_per_launch": flop})
 
     cpu = None
