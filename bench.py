@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     p.add_argument("--narrow-waves", type=int, default=0, help="plan option (0 = library default)")
     p.add_argument("--min-wave-keys", type=int, default=0, help="plan option (0 = library default)")
+    p.add_argument("--wide-tiles", type=int, default=-1, help="plan option: -1 auto, 0 never, 1 always")
     p.add_argument("--hbm-probe", action="store_true",
                    help="only measure plain streaming read and copy rates with torch kernels")
     p.add_argument("--copy-calibration", action="store_true",
@@ -147,7 +148,7 @@ def main():
     plan = pkv.pkv_plan(batch.cu_seqlens_q, batch.seq_lens, batch.num_q_heads, batch.num_kv_heads,
                         batch.head_dim, block_tables=batch.block_tables, num_blocks=batch.num_blocks,
                         options={"narrow_waves": args.narrow_waves, "min_wave_keys": args.min_wave_keys,
-                                 "wide_tiles": -1},
+                                 "wide_tiles": args.wide_tiles},
                         device=dev, stream=stream)
     slots = torch.empty(batch.num_rows, dtype=torch.int64, device=dev)
     out = torch.empty_like(t["q"])
