@@ -44,7 +44,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace"])
+    p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
+    p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     p.add_argument("--narrow-waves", type=int, default=0, help="plan option (0 = library default)")
@@ -139,6 +141,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "trace":
+        run_trace(args)
+        return
     dev = torch.device("cuda", 0)
     pkv.load_library()
     batch = getattr(wl, WORKLOADS[args.workload])()
@@ -227,6 +232,105 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def run_trace(args):
+    """The continuous-batching trace: the seeded scheduler's steps, each one
+    packed step (pkv_paged_step: slot translation + append, attention,
+    merge) for every layer, each layer with its own 65,536-block K and V
+    caches.  Each step's per-layer Q/K/V are N(0,1) drawn on the device
+    before its timed region; HIP events bracket the step's layer loop."""
+    import torch
+    import paged_kv_cache_149_amd as pkv
+    from paged_kv_cache_149_amd import accounting
+    from synth import scheduler as sc
+
+    dev = torch.device("cuda", 0)
+    pkv.load_library()
+    cfg = sc.TraceConfig(steps=args.trace_steps)
+    steps, sch = sc.continuous_batching_trace(cfg)
+    L, Hq, Hkv, D, NB = args.layers, 32, 8, 128, cfg.num_blocks
+    log(f"trace: {len(steps)} steps, {L} layers, {NB}-block pool per layer, "
+        f"{sch.preemptions} preemptions, {len(sch.finished)} requests finished")
+    kc = [torch.empty(NB, Hkv, 16, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    vc = [torch.empty(NB, Hkv, D, 16, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    Tmax = max(st.num_rows for st in steps)
+    qa = torch.empty(L, Tmax, Hq, D, dtype=torch.bfloat16, device=dev)
+    ka = torch.empty(L, Tmax, Hkv, D, dtype=torch.bfloat16, device=dev)
+    va = torch.empty(L, Tmax, Hkv, D, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(Tmax, Hq, D, dtype=torch.bfloat16, device=dev)
+    slots = torch.empty(Tmax, dtype=torch.int64, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    stream = torch.cuda.current_stream(dev)
+    scale = 1.0 / (D ** 0.5)
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    plans, events, recs = [], [], []
+    for i, st in enumerate(steps):
+        T = st.num_rows
+        qa[:, :T].normal_(generator=gen)
+        ka[:, :T].normal_(generator=gen)
+        va[:, :T].normal_(generator=gen)
+        plan = pkv.pkv_plan(st.cu_seqlens_q, st.seq_lens, Hq, Hkv, D, block_tables=st.block_tables,
+                            num_blocks=NB, device=dev, workspace=ws, stream=stream)
+        ws = plan.workspace
+        cu = torch.from_numpy(st.cu_seqlens_q).to(dev)
+        sl = torch.from_numpy(st.seq_lens).to(dev)
+        bt = torch.from_numpy(np.ascontiguousarray(st.block_tables)).to(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for l in range(L):
+            pkv.pkv_paged_step(qa[l, :T], ka[l, :T], va[l, :T], kc[l], vc[l], cu, sl, bt, scale, plan,
+                               slot_mapping=slots[:T], out=out[:T], stream=stream)
+        b.record(stream)
+        plans.append(plan)
+        events.append((a, b))
+        nbytes = accounting.step_bytes(st.cu_seqlens_q, st.seq_lens, st.block_tables, Hq, Hkv, D)
+        flop = accounting.attention_flop(st.cu_seqlens_q, st.seq_lens, Hq, D)
+        recs.append((T, st.n_decode, nbytes["total"] + nbytes["append"], nbytes["kv_unique"], flop))
+        if i % 50 == 0:
+            log(f"step {i}: {T} rows ({st.n_decode} decode), {len(st.rows)} sequences")
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in events])
+    rows = np.array([r[0] for r in recs])
+    byts = np.array([r[2] for r in recs], dtype=np.float64) * L
+    kvb = np.array([r[3] for r in recs], dtype=np.float64) * L
+    flop = np.array([r[4] for r in recs], dtype=np.float64) * L
+    t_hbm = byts / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    sec = ms * 1e-3
+    dec = t_hbm >= t_mfma
+    pre = ~dec
+    res = {
+        "metric": METRIC,
+        "value": round(kvb.sum() / sec.sum() / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": len(steps),
+        "warmup": 0,
+        "ms_per_step": round(float(ms.mean()), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"cb-trace-{len(steps)}steps-{L}layers", "layers": L, "budget": cfg.token_budget,
+                   "pool_blocks": NB, "arrival_rate": cfg.arrival_rate, "preemptions": sch.preemptions,
+                   "finished": len(sch.finished)},
+        "query_tok_s": round(rows.sum() / sec.sum(), 1),
+        "total_rows": int(rows.sum()),
+        "total_ms": round(float(ms.sum()), 3),
+        "roofline_fraction": round(float(np.maximum(t_hbm, t_mfma).sum() / sec.sum()), 4),
+        "decode_heavy": {"steps": int(dec.sum()),
+                         "hbm_frac": round(float(byts[dec].sum() / sec[dec].sum() / (HBM_PEAK_GBS * 1e9)), 4)
+                         if dec.any() else None},
+        "prefill_heavy": {"steps": int(pre.sum()),
+                          "mfma_frac": round(float(flop[pre].sum() / sec[pre].sum() / (BF16_MFMA_PEAK_TFLOPS * 1e12)), 4)
+                          if pre.any() else None,
+                          "ms": round(float(ms[pre].sum()), 3) if pre.any() else None},
+        "per_step_ms_first": [round(float(x), 3) for x in ms[:8]],
+    }
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(batch, seconds, nbytes):

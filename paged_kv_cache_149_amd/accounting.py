@@ -59,17 +59,21 @@ def kv_bytes_unique(cu_seqlens_q, seq_lens, block_tables, num_kv_heads: int, hea
     summed, times the per-token bytes."""
     ql = np.diff(np.asarray(cu_seqlens_q, dtype=np.int64))
     sl = np.asarray(seq_lens, dtype=np.int64)
-    bt = np.asarray(block_tables)
-    used = {}
-    for s in np.nonzero(ql > 0)[0]:
-        n = int(sl[s])
-        nb = (n + 15) // 16
-        for i in range(nb):
-            b = int(bt[s, i])
-            u = min(16, n - 16 * i)
-            if used.get(b, 0) < u:
-                used[b] = u
-    return sum(used.values()) * kv_bytes_per_token(num_kv_heads, head_dim)
+    bt = np.asarray(block_tables, dtype=np.int64)
+    act = np.nonzero(ql > 0)[0]
+    if act.size == 0:
+        return 0
+    nblk = (sl[act] + 15) // 16
+    idx = np.arange(bt.shape[1])[None, :]
+    mask = idx < nblk[:, None]
+    used_tokens = np.clip(sl[act][:, None] - 16 * idx, 0, 16)
+    blocks = bt[act][mask]
+    tokens = used_tokens[mask]
+    order = np.argsort(blocks, kind="stable")
+    b_sorted, t_sorted = blocks[order], tokens[order]
+    starts = np.concatenate([[0], np.nonzero(np.diff(b_sorted))[0] + 1])
+    per_block_max = np.maximum.reduceat(t_sorted, starts) if b_sorted.size else np.zeros(0)
+    return int(per_block_max.sum()) * kv_bytes_per_token(num_kv_heads, head_dim)
 
 
 def step_bytes(cu_seqlens_q, seq_lens, block_tables, num_q_heads: int, num_kv_heads: int,

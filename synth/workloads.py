@@ -267,6 +267,32 @@ def make_batch(
     )
 
 
+def batch_from_metadata(name: str, cu_seqlens_q, seq_lens, block_tables, num_blocks: int, *, seed: int,
+                        num_q_heads: int = NUM_Q_HEADS, num_kv_heads: int = NUM_KV_HEADS,
+                        head_dim: int = HEAD_DIM, unused_fill: str = "nan") -> Batch:
+    """A batch with given metadata (e.g. one step of the scheduler's trace)
+    and freshly drawn values: the step's rows, and a pool whose every
+    referenced tile is an N(0,1) draw."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int32)
+    sl = np.asarray(seq_lens, dtype=np.int32)
+    bt = np.asarray(block_tables, dtype=np.int32)
+    T = int(cu[-1])
+    rows = lambda stream, H: counter.normal_bf16_range_np(seed, stream, 0, T * H * head_dim).reshape(T, H, head_dim)
+    referenced = np.zeros(num_blocks, dtype=bool)
+    for s_ in range(sl.shape[0]):
+        nb = (int(sl[s_]) + BLOCK_SIZE - 1) // BLOCK_SIZE
+        referenced[bt[s_, :nb]] = True
+    tile = BLOCK_SIZE * head_dim
+    return Batch(
+        name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        cu_seqlens_q=cu, seq_lens=sl, block_tables=bt, num_blocks=int(num_blocks),
+        q=rows(STREAM_Q, num_q_heads), k_new=rows(STREAM_K_NEW, num_kv_heads),
+        v_new=rows(STREAM_V_NEW, num_kv_heads),
+        k_pool=Pool(seed, STREAM_K_POOL, num_blocks, num_kv_heads, tile, referenced, unused_fill),
+        v_pool=Pool(seed, STREAM_V_POOL, num_blocks, num_kv_heads, tile, referenced, unused_fill),
+        scale=np.float32(1.0 / math.sqrt(head_dim)), seed=seed)
+
+
 def permute_placement(batch: Batch, seed: int) -> Batch:
     """Same logical K/V, new physical placement: whole tiles move to new block
     ids and every block-table entry is renamed the same way."""

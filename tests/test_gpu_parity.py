@@ -239,3 +239,27 @@ def test_attention_entry_points_agree(dev):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     check_attention(pkv.bf16_bits(o2), oracle.packed_attention(b), "split entry points")
+
+
+def test_trace_sampled_steps(dev):
+    """Steps of the continuous-batching trace (65,536-block pool): each
+    step's metadata with freshly drawn values; sampled rows of every kind."""
+    from synth import scheduler as sc
+    steps, _ = sc.continuous_batching_trace(sc.TraceConfig(steps=61))
+    rng = np.random.default_rng(9)
+    for i in (0, 1, 5, 60):
+        st = steps[i]
+        b = wl.batch_from_metadata(f"trace-step{i}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
+                                   65536, seed=149005 + 1000 * i)
+        note(f"trace step {i}: {b.num_rows} rows, {b.num_seqs} sequences")
+        out, slots, t, plan = run_step(b, dev)
+        check_append(b, slots, t)
+        cu = b.cu_seqlens_q
+        rows = set(rng.integers(0, b.num_rows, size=24).tolist())
+        for s in rng.integers(0, b.num_seqs, size=6):
+            rows |= {int(cu[s]), int(cu[s + 1]) - 1}
+        rows = sorted(rows)
+        ref = oracle.packed_attention_rows(b, rows)
+        check_attention(out[rows], np.stack([ref[r] for r in rows]), f"trace step {i} (sampled)")
+        del t
+        torch.cuda.empty_cache()
