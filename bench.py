@@ -36,6 +36,8 @@ WORKLOADS = {
     "worked": "config_worked_step",
     "mixed": "config_mixed_chunked",
     "longshared": "config_long_shared",
+    "prefillchunk": "config_prefill_chunk",
+    "prefillfresh": "config_prefill_fresh",
 }
 
 

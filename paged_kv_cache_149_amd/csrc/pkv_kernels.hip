@@ -25,6 +25,8 @@
 // transposes: every operand comes straight from HBM in its MFMA layout.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -65,6 +67,25 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
+
+// Max / sum over lanes l and l^16 (resp. l^32) with gfx950's
+// v_permlane16/32_swap on a copy of the value: VALU only, no LDS round trip.
+// Written as one asm block: the builtins' results are folded incorrectly
+// when both operands hold the same value, and the s_nop's cover the VALU
+// write -> permlane read hazard that inline asm hides from the compiler.
+#define PKV_XLANE(name, perm, op)                                                        \
+  __device__ __forceinline__ float name(float v) {                                      \
+    float t;                                                                            \
+    asm volatile("v_mov_b32 %1, %0\n\ts_nop 1\n\t" perm " %0, %1\n\ts_nop 1\n\t" op \
+                 " %0, %0, %1"                                                          \
+                 : "+v"(v), "=&v"(t));                                                  \
+    return v;                                                                           \
+  }
+PKV_XLANE(xmax16, "v_permlane16_swap_b32", "v_max_f32")
+PKV_XLANE(xmax32, "v_permlane32_swap_b32", "v_max_f32")
+PKV_XLANE(xsum16, "v_permlane16_swap_b32", "v_add_f32")
+PKV_XLANE(xsum32, "v_permlane32_swap_b32", "v_add_f32")
+#undef PKV_XLANE
 
 __device__ inline float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ inline float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
@@ -316,8 +337,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
         sv[j] = ok ? sv[j] : neg_inf();
         mx = fmaxf(mx, sv[j]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = xmax32(xmax16(mx));
       const float m_new = fmaxf(m_run[nt], mx);
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
@@ -369,8 +389,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
   // ---- epilogue
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = xsum32(xsum16(l_run[nt]));
     if (!col_ok[nt]) continue;
     const int col = nt * 16 + r;
     if (it.part < 0) {
@@ -408,22 +427,315 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
   return it;
 }
 
-// Workgroup b < num_wide runs wide item b; workgroup num_wide + w walks the
-// items of narrow wavefront w in order.
-template <bool kWide>
-__device__ __forceinline__ void attention_body(const AttnArgs &a) {
-  const int b = blockIdx.x;
-  if (kWide && b < a.num_wide) {
-    const Item it = load_item(a, b);
-    if (it.k1 > it.k0 && it.np > 0) {
-      if ((it.np << a.log2G) > pkv::kTileCols)
-        run_item<4>(a, it);
-      else
-        run_item<1>(a, it);
+// ---------------------------------------------------------------------------
+// Wide prefill tile: one workgroup of four wavefronts over one (sequence, kv
+// head) and up to 4 x 64/G query positions; wavefront w owns positions
+// [w*64/G, (w+1)*64/G) of the tile, i.e. 64 columns (positions x heads).
+// Each 32-key K/V chunk (16 KiB) is staged once per workgroup in LDS with
+// direct global->LDS loads, laid out in MFMA operand order: region R (1 KiB)
+// holds, at byte 16*l, the 16 bytes lane l needs -- K operand (m-tile R/4,
+// 32-dim step R%4) for R < 8, V^T operand (16-dim tile R-8) for R >= 8.
+// Wavefront w loads regions 4w..4w+3.  Three buffers rotate: the loads of
+// chunk c+2 are in flight while chunk c is computed, one barrier per chunk.
+// ---------------------------------------------------------------------------
+constexpr int kChunkVec = 1024;  // u32x4 per chunk buffer (16 KiB)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Three distinct LDS objects (not one array) so the compiler's wait-count
+// tracking can tell a load in flight into one buffer from reads of another.
+__shared__ __attribute__((aligned(16))) u32x4 lds_chunk0[kChunkVec];
+__shared__ __attribute__((aligned(16))) u32x4 lds_chunk1[kChunkVec];
+__shared__ __attribute__((aligned(16))) u32x4 lds_chunk2[kChunkVec];
+
+template <int I>
+__device__ __forceinline__ u32x4 *lds_chunk() {
+  return I == 0 ? lds_chunk0 : (I == 1 ? lds_chunk1 : lds_chunk2);
+}
+
+// The 16 operand regions of a staged chunk, lane `lane`'s 16 bytes each.
+// Issued as plain ds_read_b128 instructions: the caller has already waited
+// for the chunk's loads (vmcnt) and passed the workgroup barrier, which the
+// compiler's own wait insertion cannot see across three rotating buffers.
+#define PKV_DS_READ(dst, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(dst) : "v"(addr))
+__device__ __forceinline__ void lds_read_operands(const u32x4 *buf, int lane, u32x4 (&k)[8],
+                                                  u32x4 (&v)[8]) {
+  const uint32_t addr =
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) u32x4 *)buf + lane);
+  PKV_DS_READ(k[0], 0);
+  PKV_DS_READ(k[1], 1024);
+  PKV_DS_READ(k[2], 2048);
+  PKV_DS_READ(k[3], 3072);
+  PKV_DS_READ(k[4], 4096);
+  PKV_DS_READ(k[5], 5120);
+  PKV_DS_READ(k[6], 6144);
+  PKV_DS_READ(k[7], 7168);
+  PKV_DS_READ(v[0], 8192);
+  PKV_DS_READ(v[1], 9216);
+  PKV_DS_READ(v[2], 10240);
+  PKV_DS_READ(v[3], 11264);
+  PKV_DS_READ(v[4], 12288);
+  PKV_DS_READ(v[5], 13312);
+  PKV_DS_READ(v[6], 14336);
+  PKV_DS_READ(v[7], 15360);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+#undef PKV_DS_READ
+
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt vmcnt(kVm), expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14));
+}
+
+__device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it) {
+  constexpr int NT = 4;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int G = 1 << a.log2G;
+  const int WP = pkv::kWideCols >> a.log2G;  // positions per wavefront
+  const int wpos0 = it.pos0 + w * WP;         // first position of this wavefront
+  const int wnp = max(0, min(WP, it.np - w * WP));
+  const int wlast = wpos0 + wnp - 1;          // last position (wnp > 0)
+
+  bool col_ok[NT];
+  int col_pos[NT];
+  int64_t col_qoff[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = nt * 16 + r;
+    const int pc = col >> a.log2G;
+    const int ho = col & (G - 1);
+    col_ok[nt] = pc < wnp;
+    col_pos[nt] = wpos0 + pc;
+    col_qoff[nt] = ((int64_t)(it.t0 + w * WP + pc) * a.Hq + it.kvh * G + ho) * D;
+  }
+  u32x4 qb[NT][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[nt][c] = col_ok[nt] ? load16(a.q + col_qoff[nt] + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+
+  f32x4 acc[NT][8], lacc[NT];
+  float m_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = neg_inf();
+    lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // A operand whose row 0 is all ones: C row 0 of ones . P^T is the column sum of P
+  const uint32_t one2 = r == 0 ? 0x3F803F80u : 0u;
+  const u32x4 ones = u32x4{one2, one2, one2, one2};
+
+  const int32_t *btrow = a.bt + (int64_t)it.seq * a.bt_stride;
+  const int kb0 = it.k0 >> 4;
+  const int kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
+  auto block_id = [&](int lb) -> int { return lb < kb_end ? sload(btrow, lb) : -1; };
+  const int nchunks = (it.k1 - it.k0 + 31) >> 5;
+  const int64_t head_off = (int64_t)it.kvh * TILE;
+  const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+  const int ka = r >> 2, kbb = r & 3;
+  const int k_sel = ka >> 1;
+  const int k_row_off = (8 * (ka & 1) + kbb) * D + 8 * g;
+  const int v_sel = g >> 1;
+  const int v_off = r * pkv::kBlock + 8 * (g & 1);
+  const float c2 = a.scale_log2;
+
+  // issue this wavefront's four regions of chunk cc into buf; returns the
+  // chunk's out-of-range flags (bit 0: first block, bit 1: needed second block)
+  auto issue = [&](int cc, u32x4 *buf) -> int {
+    const int key0 = it.k0 + 32 * cc;
+    const bool need1 = key0 + 16 < it.k1;
+    const int b0 = block_id(kb0 + 2 * cc);
+    const int b1 = need1 ? block_id(kb0 + 2 * cc + 1) : -1;
+    const bool ok0 = b0 >= 0 && b0 < a.num_blocks;
+    const bool ok1 = b1 >= 0 && b1 < a.num_blocks;
+    const int64_t t0 = (ok0 ? (int64_t)b0 * blk_stride : 0) + head_off;
+    const int64_t t1 = need1 && ok1 ? (int64_t)b1 * blk_stride + head_off : t0;
+    if (w < 2) {
+      const uint16_t *kp = a.kc + (k_sel ? t1 : t0) + k_row_off + 4 * w * D;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        __builtin_amdgcn_global_load_lds(kp + 32 * c, (lds_void_t *)(buf + (4 * w + c) * 64), 16, 0, 0);
+    } else {
+      const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off + (w - 2) * 4 * 16 * pkv::kBlock;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        __builtin_amdgcn_global_load_lds(vp + d * 16 * pkv::kBlock,
+                                         (lds_void_t *)(buf + (8 + 4 * (w - 2) + d) * 64), 16, 0, 0);
     }
+    return (ok0 ? 0 : 1) | (need1 && !ok1 ? 2 : 0);
+  };
+
+  auto compute = [&](int cc, const u32x4 *buf, int bad) {
+    const int key0 = it.k0 + 32 * cc;
+    if (wnp <= 0 || key0 > wlast) return;  // every key of the chunk is in this wavefront's future
+    const int kl = key0 + 8 * g;
+    u32x4 kop[8], vop[8];
+    lds_read_operands(buf, lane, kop, vop);
+    if (bad) {
+      const bool kz = k_sel ? (bad & 2) : (bad & 1);
+      const bool vz = v_sel ? (bad & 2) : (bad & 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (kz) kop[i] = u32x4{0, 0, 0, 0};
+        if (vz) vop[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (key0 + 32 > it.k1) {
+      const int nv = it.k1 - kl;
+      u32x4 keep;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
+    }
+    // causal masking is needed only where a key can lie past a column's
+    // position (or past the tile, or on empty columns)
+    const bool masked = key0 + 31 > wpos0 || wnp < WP || key0 + 32 > it.k1;
+    // phase 1: all S^T tiles, eight independent accumulation chains
+    f32x4 sc[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        sc[nt][0] = mfma(kop[c], qb[nt][c], sc[nt][0]);
+        sc[nt][1] = mfma(kop[4 + c], qb[nt][c], sc[nt][1]);
+      }
+    // phase 2: masking and per-lane maxima of every column tile
+    float sv[NT][8], mx[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[nt][i] = sc[nt][0][i];
+        sv[nt][4 + i] = sc[nt][1][i];
+      }
+      if (masked) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = kl + j;
+          sv[nt][j] = (col_ok[nt] && key < it.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
+        }
+      }
+      mx[nt] = sv[nt][0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mx[nt] = fmaxf(mx[nt], sv[nt][j]);
+    }
+    // phase 3: column maxima across the four lane groups
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax16(mx[nt]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax32(mx[nt]);
+    // phase 4: running max (moves only when it grows by more than 8 in the
+    // scaled base-2 domain: probabilities stay <= 2^8 and the normaliser
+    // absorbs the constant), probabilities in bf16
+    u32x4 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mxs = mx[nt] == neg_inf() ? neg_inf() : mx[nt] * c2;
+      const bool grow = mxs > m_run[nt] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mxs : m_run[nt];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - (m_new == neg_inf() ? 0.f : m_new));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+        lacc[nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+      const float m_use = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pb[nt][i] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i], c2, -m_use)),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i + 1], c2, -m_use)));
+    }
+    // phase 5: O^T += V^T P^T and the column sums
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(vop[dt], pb[nt], acc[nt][dt]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma(ones, pb[nt], lacc[nt]);
+  };
+
+  // one step: chunk cc's loads complete (the next chunk's may still fly),
+  // barrier, refill the buffer freed by chunk cc-1 with chunk cc+2, compute
+  int bad[3] = {0, 0, 0};
+  auto step = [&](int cc, auto cur_tag, auto refill_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    constexpr int REF = decltype(refill_tag)::value;
+    if (cc + 1 < nchunks)
+      wait_vmcnt<4>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (cc + 2 < nchunks) bad[REF] = issue(cc + 2, lds_chunk<REF>());
+    compute(cc, lds_chunk<CUR>(), bad[CUR]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+
+  bad[0] = issue(0, lds_chunk<0>());
+  if (nchunks > 1) bad[1] = issue(1, lds_chunk<1>());
+  for (int cc = 0; cc < nchunks; cc += 3) {
+    step(cc, I0{}, I2{});
+    if (cc + 1 < nchunks) step(cc + 1, I1{}, I0{});
+    if (cc + 2 < nchunks) step(cc + 2, I2{}, I1{});
+  }
+  // no wavefront may leave while others still read the buffers it loaded
+  __builtin_amdgcn_s_barrier();
+
+  // epilogue: column sums sit in row 0 (lanes 0..15, element 0)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float l_tot = __shfl(lacc[nt][0], r);
+    if (!col_ok[nt]) continue;
+    const float inv = 1.f / l_tot;
+    uint16_t *op = a.out + col_qoff[nt] + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 v = acc[nt][dt] * inv;
+      u32x2 o;
+      o[0] = pack_bf16(v[0], v[1]);
+      o[1] = pack_bf16(v[2], v[3]);
+      *reinterpret_cast<u32x2 *>(op + 16 * dt) = o;
+    }
+  }
+}
+
+// Narrow tiles only (decode rows and prefill tails): two waves per SIMD.
+// Workgroup w walks the items of narrow wavefront w in order.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attention_kernel(AttnArgs a) {
+  const int w = blockIdx.x;
+  if (w >= a.num_waves) return;
+  const int i0 = sload(a.waves, w);
+  const int i1 = sload(a.waves, w + 1);
+  for (int i = i0; i < i1; ++i) {
+    const Item it = load_item(a, i);
+    if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
+  }
+}
+
+// Mixed launch: workgroups [0, num_wide) run wide prefill tiles (four
+// wavefronts sharing K/V through LDS); the rest carry four narrow
+// wavefronts each, walking their item shares.
+__global__ __launch_bounds__(256) void attention_mixed_kernel(AttnArgs a) {
+  const int b = blockIdx.x;
+  if (b < a.num_wide) {
+    const Item it = load_item(a, b);
+    if (it.k1 > it.k0 && it.np > 0) run_wide_tile(a, it);
     return;
   }
-  const int w = b - (kWide ? a.num_wide : 0);
+  const int w = (b - a.num_wide) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w >= a.num_waves) return;
   const int i0 = a.num_wide + sload(a.waves, w);
   const int i1 = a.num_wide + sload(a.waves, w + 1);
@@ -431,17 +743,6 @@ __device__ __forceinline__ void attention_body(const AttnArgs &a) {
     const Item it = load_item(a, i);
     if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
   }
-}
-
-// Narrow tiles only (decode rows and prefill tails): two waves per SIMD.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attention_kernel(AttnArgs a) {
-  attention_body<false>(a);
-}
-
-// Wide prefill tiles and narrow items in the same launch.
-__global__ __launch_bounds__(64) void attention_mixed_kernel(AttnArgs a) {
-  attention_body<true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,8 +875,8 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
   if (plan->num_wide_items > 0)
-    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_wide_items + plan->num_waves), dim3(64),
-                       0, as_stream(stream), a);
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_wide_items + (plan->num_waves + 3) / 4),
+                       dim3(256), 0, as_stream(stream), a);
   else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();

@@ -5,7 +5,8 @@
 //  * q_len > 1 (prefill / chunked prefill, causal offset = cached prefix:
 //    "Continuous Batching 深入实现", section "一个 chunked prefill 请求怎么组织
 //    attention"): tiles of query positions x the kv head's query heads.  A
-//    wide tile (64 columns) is one wavefront's whole item, placed first.
+//    wide tile (up to 4 x 64/G positions: four wavefronts of 64 columns
+//    sharing K/V through LDS) is one workgroup's whole item, placed first.
 //  * Decode rows and the short tails of prefill rows: narrow (<= 16 column)
 //    units (tile, kv head), each a stream of 32-key chunks.  All chunks of all
 //    units are dealt out in equal contiguous shares to a fixed number of
@@ -94,7 +95,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     while (j < ql) {
       const int left = ql - j;
       const bool wide = use_wide && left > narrow_pos;
-      const int np = std::min(left, wide ? wide_pos : narrow_pos);
+      const int np = std::min(left, wide ? 4 * wide_pos : narrow_pos);
       Tile t{s, h_cu[s] + j, np, c + j, c + j + np, wide};
       (wide ? wide_tiles : narrow_tiles).push_back(t);
       j += np;

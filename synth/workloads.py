@@ -352,3 +352,16 @@ def config_long_shared(seed: int = CONFIG_SEEDS[4], n_seqs: int = 16, cached: in
     groups = [(tuple(range(g, min(g + group, n_seqs))), nb) for g in range(0, n_seqs, group)]
     return make_batch("longctx-16x32768-shared2048", [(cached, 1)] * n_seqs,
                       seed=seed, shared_groups=groups, **kw)
+
+
+def config_prefill_chunk(seed: int = 149006, past: int = 30720, chunk: int = 2048, **kw) -> Batch:
+    """Prefill-heavy: one 2048-token chunk continuing a 30,720-token cached
+    prefix -- the sixteenth chunk of the 32,768-token prompt of "11.2 连续批处理
+    与 PagedAttention", section 11.2.5."""
+    return make_batch(f"prefill-chunk{chunk}-after{past}", [(past, chunk)], seed=seed, **kw)
+
+
+def config_prefill_fresh(seed: int = 149007, n: int = 4, length: int = 2048, **kw) -> Batch:
+    """Prefill-heavy: four 2048-token prompts with nothing cached (an 8192-token
+    budget of fresh prefill)."""
+    return make_batch(f"prefill-{n}x{length}-fresh", [(0, length)] * n, seed=seed, **kw)

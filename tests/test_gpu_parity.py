@@ -133,6 +133,27 @@ def test_long_shared_sampled_rows(dev):
     check_attention(out[rows], np.stack([ref[r] for r in rows]), "long shared (sampled)")
 
 
+def test_prefill_chunk_sampled_rows(dev):
+    """The 2048-row chunk after 30,720 cached tokens (wide workgroup tiles)."""
+    b = wl.config_prefill_chunk()
+    note("prefill chunk: 2048 rows after 30720 cached (sampled)")
+    out, slots, t, plan = run_step(b, dev)
+    assert plan.num_wide_items > 0
+    check_append(b, slots, t)
+    rows = [0, 1, 15, 16, 63, 64, 100, 511, 1000, 1024, 1535, 2000, 2046, 2047]
+    ref = oracle.packed_attention_rows(b, rows)
+    check_attention(out[rows], np.stack([ref[r] for r in rows]), "prefill chunk (sampled)")
+
+
+def test_prefill_fresh_full(dev):
+    b = wl.make_batch("prefill-3x300", [(0, 300), (0, 257), (0, 64)], seed=35)
+    note("fresh prefills 300/257/64 (whole)")
+    out, slots, t, plan = run_step(b, dev)
+    assert plan.num_wide_items > 0
+    check_append(b, slots, t)
+    check_attention(out, oracle.packed_attention(b), "fresh prefills")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_placement_invariance_bitwise(dev):
