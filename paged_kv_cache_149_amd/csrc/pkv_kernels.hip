@@ -25,8 +25,6 @@
 // transposes: every operand comes straight from HBM in its MFMA layout.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
 #include "pkv_internal.h"
 
 namespace {
@@ -441,26 +439,22 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
 constexpr int kChunkVec = 1024;  // u32x4 per chunk buffer (16 KiB)
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Three distinct LDS objects (not one array) so the compiler's wait-count
-// tracking can tell a load in flight into one buffer from reads of another.
-__shared__ __attribute__((aligned(16))) u32x4 lds_chunk0[kChunkVec];
-__shared__ __attribute__((aligned(16))) u32x4 lds_chunk1[kChunkVec];
-__shared__ __attribute__((aligned(16))) u32x4 lds_chunk2[kChunkVec];
+// Three rotating chunk buffers, and the workgroup's recompute flag.
+__shared__ __attribute__((aligned(16))) u32x4 lds_chunks[3 * kChunkVec];
+__shared__ int lds_restart;
 
-template <int I>
-__device__ __forceinline__ u32x4 *lds_chunk() {
-  return I == 0 ? lds_chunk0 : (I == 1 ? lds_chunk1 : lds_chunk2);
-}
-
-// The 16 operand regions of a staged chunk, lane `lane`'s 16 bytes each.
-// Issued as plain ds_read_b128 instructions: the caller has already waited
-// for the chunk's loads (vmcnt) and passed the workgroup barrier, which the
-// compiler's own wait insertion cannot see across three rotating buffers.
+// Operand regions of a staged chunk, lane `lane`'s 16 bytes each: the K
+// operands (regions 0..7) and, separately, the V^T operands (regions 8..15),
+// so the V reads can land while the scores are computed.  Issued as plain
+// ds_read_b128 instructions: the caller has already waited for the chunk's
+// loads (vmcnt) and passed the workgroup barrier, which the compiler's own
+// wait insertion cannot see across three rotating buffers; the caller
+// waits on lgkmcnt before using the results.
 #define PKV_DS_READ(dst, off) asm volatile("ds_read_b128 %0, %1 offset:" #off : "=v"(dst) : "v"(addr))
-__device__ __forceinline__ void lds_read_operands(const u32x4 *buf, int lane, u32x4 (&k)[8],
-                                                  u32x4 (&v)[8]) {
-  const uint32_t addr =
-      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) u32x4 *)buf + lane);
+__device__ __forceinline__ uint32_t lds_lane_addr(const u32x4 *buf, int lane) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) u32x4 *)buf + lane);
+}
+__device__ __forceinline__ void lds_read_k(uint32_t addr, u32x4 (&k)[8]) {
   PKV_DS_READ(k[0], 0);
   PKV_DS_READ(k[1], 1024);
   PKV_DS_READ(k[2], 2048);
@@ -469,6 +463,8 @@ __device__ __forceinline__ void lds_read_operands(const u32x4 *buf, int lane, u3
   PKV_DS_READ(k[5], 5120);
   PKV_DS_READ(k[6], 6144);
   PKV_DS_READ(k[7], 7168);
+}
+__device__ __forceinline__ void lds_read_v(uint32_t addr, u32x4 (&v)[8]) {
   PKV_DS_READ(v[0], 8192);
   PKV_DS_READ(v[1], 9216);
   PKV_DS_READ(v[2], 10240);
@@ -477,8 +473,8 @@ __device__ __forceinline__ void lds_read_operands(const u32x4 *buf, int lane, u3
   PKV_DS_READ(v[5], 13312);
   PKV_DS_READ(v[6], 14336);
   PKV_DS_READ(v[7], 15360);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 #undef PKV_DS_READ
 
 template <int kVm>
@@ -518,15 +514,16 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
     for (int c = 0; c < 4; ++c)
       qb[nt][c] = col_ok[nt] ? load16(a.q + col_qoff[nt] + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
 
+  // Probabilities are taken relative to a fixed per-column reference: the
+  // maximum of the first chunk the column sees (key 0 is always in it).
+  // fp32 and bf16 keep 8 exponent bits, so later scores may exceed it by
+  // up to ~2^127 without overflow and nothing is ever rescaled -- the
+  // accumulators never leave the matrix cores inside the loop.  The true
+  // running maximum is tracked beside it; if any column grows past the
+  // reference by more than 2^100, the workgroup recomputes the tile with
+  // the exact maximum from the first pass (probabilities then <= 1).
   f32x4 acc[NT][8], lacc[NT];
-  float m_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = neg_inf();
-    lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  float m_ref[NT], m_hi[NT];
   // A operand whose row 0 is all ones: C row 0 of ones . P^T is the column sum of P
   const uint32_t one2 = r == 0 ? 0x3F803F80u : 0u;
   const u32x4 ones = u32x4{one2, one2, one2, one2};
@@ -573,27 +570,17 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
 
   auto compute = [&](int cc, const u32x4 *buf, int bad) {
     const int key0 = it.k0 + 32 * cc;
-    if (wnp <= 0 || key0 > wlast) return;  // every key of the chunk is in this wavefront's future
     const int kl = key0 + 8 * g;
+    const uint32_t laddr = lds_lane_addr(buf, lane);
     u32x4 kop[8], vop[8];
-    lds_read_operands(buf, lane, kop, vop);
-    if (bad) {
-      const bool kz = k_sel ? (bad & 2) : (bad & 1);
-      const bool vz = v_sel ? (bad & 2) : (bad & 1);
+    lds_read_k(laddr, kop);
+    wait_lds();
+    // table entries outside [0, num_blocks) read as zero keys and values
+    const bool kz = bad && (k_sel ? (bad & 2) : (bad & 1));
+    const bool vz = bad && (v_sel ? (bad & 2) : (bad & 1));
+    if (kz) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (kz) kop[i] = u32x4{0, 0, 0, 0};
-        if (vz) vop[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (key0 + 32 > it.k1) {
-      const int nv = it.k1 - kl;
-      u32x4 keep;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
+      for (int i = 0; i < 8; ++i) kop[i] = u32x4{0, 0, 0, 0};
     }
     // causal masking is needed only where a key can lie past a column's
     // position (or past the tile, or on empty columns)
@@ -609,6 +596,8 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
         sc[nt][0] = mfma(kop[c], qb[nt][c], sc[nt][0]);
         sc[nt][1] = mfma(kop[4 + c], qb[nt][c], sc[nt][1]);
       }
+    // the V^T operands land while the softmax runs
+    lds_read_v(laddr, vop);
     // phase 2: masking and per-lane maxima of every column tile
     float sv[NT][8], mx[NT];
 #pragma unroll
@@ -634,29 +623,35 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
     for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax16(mx[nt]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax32(mx[nt]);
-    // phase 4: running max (moves only when it grows by more than 8 in the
-    // scaled base-2 domain: probabilities stay <= 2^8 and the normaliser
-    // absorbs the constant), probabilities in bf16
+    // phase 4: probabilities in bf16 against the column's reference
     u32x4 pb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float mxs = mx[nt] == neg_inf() ? neg_inf() : mx[nt] * c2;
-      const bool grow = mxs > m_run[nt] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mxs : m_run[nt];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - (m_new == neg_inf() ? 0.f : m_new));
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
-        lacc[nt] *= alpha;
-        m_run[nt] = m_new;
-      }
-      const float m_use = m_run[nt] == neg_inf() ? 0.f : m_run[nt];
+      if (m_ref[nt] == neg_inf()) m_ref[nt] = mxs;
+      m_hi[nt] = fmaxf(m_hi[nt], mxs);
+      const float m_use = m_ref[nt] == neg_inf() ? 0.f : m_ref[nt];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         pb[nt][i] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i], c2, -m_use)),
                               __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i + 1], c2, -m_use)));
     }
     // phase 5: O^T += V^T P^T and the column sums
+    wait_lds();
+    if (vz) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vop[i] = u32x4{0, 0, 0, 0};
+    }
+    if (key0 + 32 > it.k1) {
+      // keys past the tile may hold stale data: zero their values
+      const int nv = it.k1 - kl;
+      u32x4 keep;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
+    }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -665,33 +660,61 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
     for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma(ones, pb[nt], lacc[nt]);
   };
 
-  // one step: chunk cc's loads complete (the next chunk's may still fly),
-  // barrier, refill the buffer freed by chunk cc-1 with chunk cc+2, compute
-  int bad[3] = {0, 0, 0};
-  auto step = [&](int cc, auto cur_tag, auto refill_tag) {
-    constexpr int CUR = decltype(cur_tag)::value;
-    constexpr int REF = decltype(refill_tag)::value;
-    if (cc + 1 < nchunks)
-      wait_vmcnt<4>();
-    else
-      wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (cc + 2 < nchunks) bad[REF] = issue(cc + 2, lds_chunk<REF>());
-    compute(cc, lds_chunk<CUR>(), bad[CUR]);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-
-  bad[0] = issue(0, lds_chunk<0>());
-  if (nchunks > 1) bad[1] = issue(1, lds_chunk<1>());
-  for (int cc = 0; cc < nchunks; cc += 3) {
-    step(cc, I0{}, I2{});
-    if (cc + 1 < nchunks) step(cc + 1, I1{}, I0{});
-    if (cc + 2 < nchunks) step(cc + 2, I2{}, I1{});
+  // One step: chunk cc's loads complete (the next chunk's may still fly),
+  // barrier, refill the buffer freed by chunk cc-1 with chunk cc+2, compute.
+  // f0 / f1 / f2: out-of-range flags of chunks cc, cc+1, cc+2.
+  const int ncomp = wnp > 0 ? min(nchunks, (wlast - it.k0) / 32 + 1) : 0;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // second pass: the exact maximum of the first is the reference
+      m_ref[nt] = pass == 0 ? neg_inf() : m_hi[nt];
+      if (pass == 0) m_hi[nt] = neg_inf();
+      lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (pass == 0) {
+      if (w == 0 && lane == 0) lds_restart = 0;
+      __syncthreads();
+    }
+    int f0 = issue(0, lds_chunks), f1 = 0;
+    if (nchunks > 1) f1 = issue(1, lds_chunks + kChunkVec);
+    int cur = 0;  // buffer of chunk cc
+    auto advance = [&](int cc) -> int {  // wait, barrier, refill; returns chunk cc+2's flags
+      if (cc + 1 < nchunks)
+        wait_vmcnt<4>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      const int refill = cur == 0 ? 2 : cur - 1;  // (cc + 2) % 3
+      return cc + 2 < nchunks ? issue(cc + 2, lds_chunks + refill * kChunkVec) : 0;
+    };
+    // chunks holding keys at or before this wavefront's last position are
+    // computed; later ones only keep the workgroup's loads and barriers going
+    int cc = 0;
+    for (; cc < ncomp; ++cc) {
+      const int f2 = advance(cc);
+      compute(cc, lds_chunks + cur * kChunkVec, f0);
+      f0 = f1;
+      f1 = f2;
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+    for (; cc < nchunks; ++cc) {
+      advance(cc);
+      cur = cur == 2 ? 0 : cur + 1;
+    }
+    if (pass == 1) break;
+    // did any column of any wavefront outgrow its reference by 2^100?
+    bool grew = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) grew |= m_hi[nt] > m_ref[nt] + 100.f;
+    if (__builtin_amdgcn_ballot_w64(grew) && lane == 0) atomicOr(&lds_restart, 1);
+    __syncthreads();
+    const bool again = lds_restart != 0;
+    __syncthreads();
+    if (!again) break;
   }
-  // no wavefront may leave while others still read the buffers it loaded
-  __builtin_amdgcn_s_barrier();
 
   // epilogue: column sums sit in row 0 (lanes 0..15, element 0)
 #pragma unroll
