@@ -131,7 +131,7 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * chunked prefill, whose causal offset is the cached prefix: "Continuous
  * Batching 深入实现", section "一个 chunked prefill 请求怎么组织 attention")
  * become tiles of query positions x the kv head's query heads; a wide tile
- * (64 columns) is one wavefront's item.  Everything else -- decode rows and
+ * (256 columns: up to 256/G positions) is one workgroup's item.  Everything else -- decode rows and
  * short tiles ("11.2 连续批处理与 PagedAttention", section 11.2.2: attention
  * runs per request inside one launch) -- is a (tile, kv head) unit whose
  * keys stream through the cache; all units' 32-key chunks are dealt out in
@@ -153,7 +153,8 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * plan->host_bytes then hold the sizes needed), PKV_EHIP.
  * ------------------------------------------------------------------------- */
 typedef struct pkv_plan_options {
-  int32_t narrow_waves;   /* wavefronts sharing the decode work (0 = default) */
+  int32_t narrow_waves;   /* wavefronts sharing the decode work (0 = default:
+                             1024, or 2048 when the plan has wide tiles) */
   int32_t min_wave_keys;  /* smallest share per wavefront, keys (0 = default) */
   int32_t wide_tiles;     /* -1 auto, 0 never, 1 always use wide prefill tiles */
   int32_t reserved;
@@ -162,7 +163,7 @@ typedef struct pkv_plan_options {
 typedef struct pkv_plan {
   int32_t num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim;
   int32_t num_items;      /* attention work items */
-  int32_t num_wide_items; /* wide tiles: items [0, num_wide_items), one per wavefront */
+  int32_t num_wide_items; /* wide tiles: items [0, num_wide_items), one per workgroup */
   int32_t num_waves;      /* wavefronts walking the remaining items */
   int32_t num_merge;      /* merge entries (one per split output row x head) */
   int32_t num_part_cols;  /* partial-result columns in the workspace */

@@ -11,7 +11,8 @@ namespace pkv {
 constexpr int kBlock = 16;       // tokens per paged block
 constexpr int kHeadDim = 128;    // supported head dimension
 constexpr int kTileCols = 16;    // MFMA columns of a narrow tile
-constexpr int kWideCols = 64;    // columns of a wide tile (4 MFMA column tiles)
+constexpr int kWideCols = 256;   // columns (positions x heads) of a wide tile
+constexpr int kWideWaves = 8;    // wavefronts of a wide-tile workgroup (32 columns each)
 constexpr int kChunkKeys = 32;   // keys per inner-loop step (two blocks)
 constexpr size_t kAlign = 256;
 

@@ -426,15 +426,17 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide prefill tile: one workgroup of four wavefronts over one (sequence, kv
-// head) and up to 4 x 64/G query positions; wavefront w owns positions
-// [w*64/G, (w+1)*64/G) of the tile, i.e. 64 columns (positions x heads).
-// Each 32-key K/V chunk (16 KiB) is staged once per workgroup in LDS with
-// direct global->LDS loads, laid out in MFMA operand order: region R (1 KiB)
-// holds, at byte 16*l, the 16 bytes lane l needs -- K operand (m-tile R/4,
-// 32-dim step R%4) for R < 8, V^T operand (16-dim tile R-8) for R >= 8.
-// Wavefront w loads regions 4w..4w+3.  Three buffers rotate: the loads of
-// chunk c+2 are in flight while chunk c is computed, one barrier per chunk.
+// Wide prefill tile: one workgroup of eight wavefronts over one (sequence,
+// kv head) and up to 256/G query positions; wavefront w owns positions
+// [w*32/G, (w+1)*32/G) of the tile, i.e. 32 columns (positions x heads).
+// Two wavefronts share each SIMD, so one's softmax overlaps the other's
+// matrix work.  Each 32-key K/V chunk (16 KiB) is staged once per workgroup
+// in LDS with direct global->LDS loads, laid out in MFMA operand order:
+// region R (1 KiB) holds, at byte 16*l, the 16 bytes lane l needs -- K
+// operand (m-tile R/4, 32-dim step R%4) for R < 8, V^T operand (16-dim tile
+// R-8) for R >= 8.  Wavefront w loads regions 2w, 2w+1.  Three buffers
+// rotate: the loads of chunk c+2 are in flight while chunk c is computed,
+// one barrier per chunk.
 // ---------------------------------------------------------------------------
 constexpr int kChunkVec = 1024;  // u32x4 per chunk buffer (16 KiB)
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -484,13 +486,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it) {
-  constexpr int NT = 4;
+  constexpr int WV = pkv::kWideWaves;
+  constexpr int NT = pkv::kWideCols / (16 * WV);  // MFMA column tiles per wavefront
+  constexpr int RPW = 16 / WV;                    // operand regions loaded per wavefront
+  static_assert(NT * 16 * WV == pkv::kWideCols && RPW * WV == 16, "wide tile shape");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
   const int G = 1 << a.log2G;
-  const int WP = pkv::kWideCols >> a.log2G;  // positions per wavefront
+  const int WP = (pkv::kWideCols / WV) >> a.log2G;  // positions per wavefront
   const int wpos0 = it.pos0 + w * WP;         // first position of this wavefront
   const int wnp = max(0, min(WP, it.np - w * WP));
   const int wlast = wpos0 + wnp - 1;          // last position (wnp > 0)
@@ -542,8 +547,8 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
   const int v_off = r * pkv::kBlock + 8 * (g & 1);
   const float c2 = a.scale_log2;
 
-  // issue this wavefront's four regions of chunk cc into buf; returns the
-  // chunk's out-of-range flags (bit 0: first block, bit 1: needed second block)
+  // issue this wavefront's regions of chunk cc into buf; returns the chunk's
+  // out-of-range flags (bit 0: first block, bit 1: needed second block)
   auto issue = [&](int cc, u32x4 *buf) -> int {
     const int key0 = it.k0 + 32 * cc;
     const bool need1 = key0 + 16 < it.k1;
@@ -553,17 +558,13 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
     const bool ok1 = b1 >= 0 && b1 < a.num_blocks;
     const int64_t t0 = (ok0 ? (int64_t)b0 * blk_stride : 0) + head_off;
     const int64_t t1 = need1 && ok1 ? (int64_t)b1 * blk_stride + head_off : t0;
-    if (w < 2) {
-      const uint16_t *kp = a.kc + (k_sel ? t1 : t0) + k_row_off + 4 * w * D;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_global_load_lds(kp + 32 * c, (lds_void_t *)(buf + (4 * w + c) * 64), 16, 0, 0);
-    } else {
-      const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off + (w - 2) * 4 * 16 * pkv::kBlock;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        __builtin_amdgcn_global_load_lds(vp + d * 16 * pkv::kBlock,
-                                         (lds_void_t *)(buf + (8 + 4 * (w - 2) + d) * 64), 16, 0, 0);
+    for (int j = 0; j < RPW; ++j) {
+      const int R = w * RPW + j;  // wavefront-uniform
+      const uint16_t *src =
+          R < 8 ? a.kc + (k_sel ? t1 : t0) + k_row_off + 4 * (R >> 2) * D + 32 * (R & 3)
+                : a.vc + (v_sel ? t1 : t0) + v_off + (R - 8) * 16 * pkv::kBlock;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + R * 64), 16, 0, 0);
     }
     return (ok0 ? 0 : 1) | (need1 && !ok1 ? 2 : 0);
   };
@@ -683,7 +684,7 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
     int cur = 0;  // buffer of chunk cc
     auto advance = [&](int cc) -> int {  // wait, barrier, refill; returns chunk cc+2's flags
       if (cc + 1 < nchunks)
-        wait_vmcnt<4>();
+        wait_vmcnt<RPW>();
       else
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
@@ -748,17 +749,17 @@ void attention_kernel(AttnArgs a) {
   }
 }
 
-// Mixed launch: workgroups [0, num_wide) run wide prefill tiles (four
-// wavefronts sharing K/V through LDS); the rest carry four narrow
+// Mixed launch: workgroups [0, num_wide) run wide prefill tiles (eight
+// wavefronts sharing K/V through LDS); the rest carry eight narrow
 // wavefronts each, walking their item shares.
-__global__ __launch_bounds__(256) void attention_mixed_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(AttnArgs a) {
   const int b = blockIdx.x;
   if (b < a.num_wide) {
     const Item it = load_item(a, b);
     if (it.k1 > it.k0 && it.np > 0) run_wide_tile(a, it);
     return;
   }
-  const int w = (b - a.num_wide) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = (b - a.num_wide) * pkv::kWideWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w >= a.num_waves) return;
   const int i0 = a.num_wide + sload(a.waves, w);
   const int i1 = a.num_wide + sload(a.waves, w + 1);
@@ -898,8 +899,9 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
   if (plan->num_wide_items > 0)
-    hipLaunchKernelGGL(attention_mixed_kernel, dim3(plan->num_wide_items + (plan->num_waves + 3) / 4),
-                       dim3(256), 0, as_stream(stream), a);
+    hipLaunchKernelGGL(attention_mixed_kernel,
+                       dim3(plan->num_wide_items + (plan->num_waves + pkv::kWideWaves - 1) / pkv::kWideWaves),
+                       dim3(64 * pkv::kWideWaves), 0, as_stream(stream), a);
   else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();

@@ -28,7 +28,11 @@ namespace {
 using pkv::Item;
 using pkv::Merge;
 
-constexpr int kDefaultNarrowWaves = 1024;   // 4 wavefronts per CU on 256 CUs
+// Narrow wavefronts: one per SIMD on 256 CUs for a narrow-only launch; in a
+// mixed launch they travel eight to a workgroup, so twice as many keep every
+// CU streaming while the wide tiles occupy some of them.
+constexpr int kDefaultNarrowWaves = 1024;
+constexpr int kDefaultNarrowWavesMixed = 2048;
 constexpr int kDefaultMinWaveKeys = 512;
 
 int round_up32(int64_t x) { return (int)((x + 31) / 32 * 32); }
@@ -72,7 +76,6 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     }
   }
 
-  const int want_waves = (opts && opts->narrow_waves > 0) ? opts->narrow_waves : kDefaultNarrowWaves;
   const int min_wave_keys = (opts && opts->min_wave_keys > 0) ? opts->min_wave_keys : kDefaultMinWaveKeys;
   const int wide_opt = opts ? opts->wide_tiles : -1;
   const int narrow_pos = pkv::kTileCols / G;  // positions per narrow tile
@@ -95,7 +98,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     while (j < ql) {
       const int left = ql - j;
       const bool wide = use_wide && left > narrow_pos;
-      const int np = std::min(left, wide ? 4 * wide_pos : narrow_pos);
+      const int np = std::min(left, wide ? wide_pos : narrow_pos);
       Tile t{s, h_cu[s] + j, np, c + j, c + j + np, wide};
       (wide ? wide_tiles : narrow_tiles).push_back(t);
       j += np;
@@ -113,6 +116,9 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   for (const Tile &t : wide_tiles)
     for (int h = 0; h < Hkv; ++h) items.push_back(Item{t.seq, h, t.t0, t.np, t.pos0, 0, t.keys, -1});
   const int n_wide = (int)items.size();
+  const int want_waves = (opts && opts->narrow_waves > 0) ? opts->narrow_waves
+                         : n_wide > 0                    ? kDefaultNarrowWavesMixed
+                                                         : kDefaultNarrowWaves;
 
   // narrow units (tile, kv head) in order; chunk counts
   const int64_t n_units = (int64_t)narrow_tiles.size() * Hkv;
