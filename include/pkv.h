@@ -170,6 +170,7 @@ typedef struct pkv_plan {
   int32_t wave_keys;      /* keys per wavefront share */
   int32_t reserved;
   int64_t items_off, waves_off, merge_off, ml_off, o_off; /* byte offsets into ws */
+  int64_t zero_off;       /* byte offset of a 4 KiB all-zero tile in ws */
   size_t ws_bytes;        /* workspace bytes this plan uses */
   size_t host_bytes;      /* host staging bytes this plan uses */
   int64_t kv_keys;        /* sum over sequences of visible keys (accounting) */
@@ -198,7 +199,8 @@ int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
  * bf16 for the P.V product and the normaliser sums those rounded values;
  * out is rounded to bf16 (nearest even).  Block-table entries outside
  * [0, num_blocks) read as zero keys/values.  Errors: PKV_EINVAL (null
- * pointers, plan mismatch), PKV_EWORKSPACE, PKV_EHIP.
+ * pointers, plan mismatch), PKV_ERANGE (num_blocks x num_kv_heads above
+ * 2^32), PKV_EWORKSPACE, PKV_EHIP.
  * ------------------------------------------------------------------------- */
 int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                               const pkv_bf16 *v_cache,

@@ -50,6 +50,7 @@ class PlanStruct(ctypes.Structure):
                 ("wave_keys", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("items_off", ctypes.c_int64), ("waves_off", ctypes.c_int64),
                 ("merge_off", ctypes.c_int64), ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
+                ("zero_off", ctypes.c_int64),
                 ("ws_bytes", ctypes.c_size_t), ("host_bytes", ctypes.c_size_t),
                 ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64)]
 

@@ -36,6 +36,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = pkv::kHeadDim;
 constexpr int TILE = pkv::kBlock * pkv::kHeadDim;  // elements of a (block, head) tile
@@ -61,10 +63,16 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 __device__ inline int32_t sload(const int32_t *p, int64_t i) { return ((const_i32 *)p)[i]; }
 
 // fp32 -> bf16 (round to nearest even), packed two per dword; low half first
+// two floats to bf16 (nearest even), lo in the low half: one v_cvt_pk_bf16_f32
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// acc + (the two bf16 halves of w), exactly as rounded: a dot product with (1, 1)
+__device__ inline float sum_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
+__device__ inline float max3(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
 // Max / sum over lanes l and l^16 (resp. l^32) with gfx950's
 // v_permlane16/32_swap on a copy of the value: VALU only, no LDS round trip.
@@ -184,6 +192,7 @@ struct AttnArgs {
   const int32_t *waves;  // item offsets of the narrow wavefronts (after the wide items)
   float2 *part_ml;
   float *part_o;
+  const uint16_t *zero;  // one all-zero (block, head) tile
   int64_t num_blocks;
   int32_t bt_stride;
   int32_t num_items;
@@ -434,15 +443,16 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
 // in LDS with direct global->LDS loads, laid out in MFMA operand order:
 // region R (1 KiB) holds, at byte 16*l, the 16 bytes lane l needs -- K
 // operand (m-tile R/4, 32-dim step R%4) for R < 8, V^T operand (16-dim tile
-// R-8) for R >= 8.  Wavefront w loads regions 2w, 2w+1.  Three buffers
-// rotate: the loads of chunk c+2 are in flight while chunk c is computed,
-// one barrier per chunk.
+// R-8) for R >= 8.  Wavefront w loads regions 2w, 2w+1.  A ring of six
+// buffers keeps the loads of up to three chunks in flight ahead of the ones
+// being computed; two barriers per chunk pace the two wavefront groups.
 // ---------------------------------------------------------------------------
 constexpr int kChunkVec = 1024;  // u32x4 per chunk buffer (16 KiB)
+constexpr int kNbuf = 8;         // chunk buffers in the ring (128 KiB)
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Three rotating chunk buffers, and the workgroup's recompute flag.
-__shared__ __attribute__((aligned(16))) u32x4 lds_chunks[3 * kChunkVec];
+// The ring of chunk buffers, and the workgroup's recompute flag.
+__shared__ __attribute__((aligned(16))) u32x4 lds_chunks[kNbuf * kChunkVec];
 __shared__ int lds_restart;
 
 // Operand regions of a staged chunk, lane `lane`'s 16 bytes each: the K
@@ -477,6 +487,17 @@ __device__ __forceinline__ void lds_read_v(uint32_t addr, u32x4 (&v)[8]) {
   PKV_DS_READ(v[7], 15360);
 }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Waits that also hand the eight operand registers just read through to
+// their users, so no use can be scheduled above the wait.  lgkmcnt(8): all
+// but the last eight LDS reads issued have returned (they return in order).
+#define PKV_OPS8(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+__device__ __forceinline__ void wait_lds_for(u32x4 (&x)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : PKV_OPS8(x)::"memory");
+}
+__device__ __forceinline__ void wait_lds_but8_for(u32x4 (&x)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(8)" : PKV_OPS8(x)::"memory");
+}
+#undef PKV_OPS8
 #undef PKV_DS_READ
 
 template <int kVm>
@@ -489,16 +510,18 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
   constexpr int WV = pkv::kWideWaves;
   constexpr int NT = pkv::kWideCols / (16 * WV);  // MFMA column tiles per wavefront
   constexpr int RPW = 16 / WV;                    // operand regions loaded per wavefront
-  static_assert(NT * 16 * WV == pkv::kWideCols && RPW * WV == 16, "wide tile shape");
+  constexpr int kAhead = kNbuf - 3;               // chunks whose loads are issued ahead
+  static_assert(NT * 16 * WV == pkv::kWideCols && RPW == 2, "wide tile shape");
+  static_assert((kNbuf & (kNbuf - 1)) == 0 && kAhead == 5, "ring of eight, waits below");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int r = lane & 15;
   const int G = 1 << a.log2G;
   const int WP = (pkv::kWideCols / WV) >> a.log2G;  // positions per wavefront
-  const int wpos0 = it.pos0 + w * WP;         // first position of this wavefront
+  const int wpos0 = it.pos0 + w * WP;                // first position of this wavefront
   const int wnp = max(0, min(WP, it.np - w * WP));
-  const int wlast = wpos0 + wnp - 1;          // last position (wnp > 0)
+  const int wlast = wpos0 + wnp - 1;                 // last position (wnp > 0)
 
   bool col_ok[NT];
   int col_pos[NT];
@@ -520,209 +543,239 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
       qb[nt][c] = col_ok[nt] ? load16(a.q + col_qoff[nt] + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
 
   // Probabilities are taken relative to a fixed per-column reference: the
-  // maximum of the first chunk the column sees (key 0 is always in it).
+  // maximum of the column's scores in the first chunk (key 0 is in it).
   // fp32 and bf16 keep 8 exponent bits, so later scores may exceed it by
   // up to ~2^127 without overflow and nothing is ever rescaled -- the
-  // accumulators never leave the matrix cores inside the loop.  The true
-  // running maximum is tracked beside it; if any column grows past the
-  // reference by more than 2^100, the workgroup recomputes the tile with
-  // the exact maximum from the first pass (probabilities then <= 1).
-  f32x4 acc[NT][8], lacc[NT];
-  float m_ref[NT], m_hi[NT];
-  // A operand whose row 0 is all ones: C row 0 of ones . P^T is the column sum of P
-  const uint32_t one2 = r == 0 ? 0x3F803F80u : 0u;
-  const u32x4 ones = u32x4{one2, one2, one2, one2};
+  // accumulators never leave the matrix cores inside the loop.  Each lane
+  // tracks the maximum of the raw scores it sees; if any column outgrows its
+  // reference by more than 2^100, the workgroup recomputes the tile with the
+  // exact maximum from the first pass as reference (probabilities then <= 1).
+  f32x4 acc[NT][8];
+  float neg_ref[NT];  // -(reference) in log2 units
+  float m_hi[NT];     // this lane's largest raw score
+  float l_part[NT];   // this lane's sum of its rounded probabilities
 
   const int32_t *btrow = a.bt + (int64_t)it.seq * a.bt_stride;
   const int kb0 = it.k0 >> 4;
   const int kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
-  auto block_id = [&](int lb) -> int { return lb < kb_end ? sload(btrow, lb) : -1; };
   const int nchunks = (it.k1 - it.k0 + 31) >> 5;
-  const int64_t head_off = (int64_t)it.kvh * TILE;
-  const int64_t blk_stride = (int64_t)a.Hkv * TILE;
-  const int ka = r >> 2, kbb = r & 3;
-  const int k_sel = ka >> 1;
-  const int k_row_off = (8 * (ka & 1) + kbb) * D + 8 * g;
-  const int v_sel = g >> 1;
-  const int v_off = r * pkv::kBlock + 8 * (g & 1);
   const float c2 = a.scale_log2;
 
-  // issue this wavefront's regions of chunk cc into buf; returns the chunk's
-  // out-of-range flags (bit 0: first block, bit 1: needed second block)
-  auto issue = [&](int cc, u32x4 *buf) -> int {
-    const int key0 = it.k0 + 32 * cc;
-    const bool need1 = key0 + 16 < it.k1;
-    const int b0 = block_id(kb0 + 2 * cc);
-    const int b1 = need1 ? block_id(kb0 + 2 * cc + 1) : -1;
-    const bool ok0 = b0 >= 0 && b0 < a.num_blocks;
-    const bool ok1 = b1 >= 0 && b1 < a.num_blocks;
-    const int64_t t0 = (ok0 ? (int64_t)b0 * blk_stride : 0) + head_off;
-    const int64_t t1 = need1 && ok1 ? (int64_t)b1 * blk_stride + head_off : t0;
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int R = w * RPW + j;  // wavefront-uniform
-      const uint16_t *src =
-          R < 8 ? a.kc + (k_sel ? t1 : t0) + k_row_off + 4 * (R >> 2) * D + 32 * (R & 3)
-                : a.vc + (v_sel ? t1 : t0) + v_off + (R - 8) * 16 * pkv::kBlock;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(buf + R * 64), 16, 0, 0);
+  // Wavefronts 0-3 load the K regions of each chunk, wavefronts 4-7 the V^T
+  // regions, two each.  A lane's two regions lie in the same block of the
+  // chunk (sel) at a fixed offset (lane_off) and region distance (imm).
+  const bool kside = w < 4;
+  const uint16_t *cache = kside ? a.kc : a.vc;
+  int sel, lane_off;
+  {
+    const int ka = r >> 2, kbb = r & 3;
+    const int R0 = w * RPW;
+    if (kside) {  // region R: m-tile R/4 (keys +4), 32-dim step R%4
+      sel = ka >> 1;
+      lane_off = (8 * (ka & 1) + kbb) * D + 8 * g + 4 * (R0 >> 2) * D + 32 * (R0 & 3);
+    } else {      // region R: 16-dim tile R-8
+      sel = g >> 1;
+      lane_off = r * pkv::kBlock + 8 * (g & 1) + (R0 - 8) * 16 * pkv::kBlock;
     }
-    return (ok0 ? 0 : 1) | (need1 && !ok1 ? 2 : 0);
+  }
+  const uint32_t nblk = (uint32_t)a.num_blocks;
+  // the (block, kv head) tile of logical block lb; table entries outside
+  // [0, num_blocks), and blocks past the item, read the all-zero tile
+  auto tile = [&](int lb) -> const uint16_t * {
+    const int b = lb < kb_end ? sload(btrow, lb) : -1;
+    return (uint32_t)b < nblk ? cache + (uint64_t)((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)it.kvh) * TILE
+                              : a.zero;
+  };
+  auto slot = [&](int c) -> u32x4 * { return lds_chunks + (c & (kNbuf - 1)) * kChunkVec; };
+  // this wavefront's two regions of chunk cc
+  auto issue = [&](int cc) {
+    const uint16_t *t0 = tile(kb0 + 2 * cc);
+    const uint16_t *t1 = tile(kb0 + 2 * cc + 1);
+    const uint16_t *src = (sel ? t1 : t0) + lane_off;
+    u32x4 *dst = slot(cc) + w * RPW * 64;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + (kside ? 32 : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0, 0);
   };
 
-  auto compute = [&](int cc, const u32x4 *buf, int bad) {
-    const int key0 = it.k0 + 32 * cc;
-    const int kl = key0 + 8 * g;
-    const uint32_t laddr = lds_lane_addr(buf, lane);
-    u32x4 kop[8], vop[8];
-    lds_read_k(laddr, kop);
-    wait_lds();
-    // table entries outside [0, num_blocks) read as zero keys and values
-    const bool kz = bad && (k_sel ? (bad & 2) : (bad & 1));
-    const bool vz = bad && (v_sel ? (bad & 2) : (bad & 1));
-    if (kz) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kop[i] = u32x4{0, 0, 0, 0};
+  // Two groups of four wavefronts (one of each per SIMD) run half a step
+  // apart.  A wavefront alternates a vector phase V(c) -- the probabilities
+  // of chunk c, while the K operands of chunk c+1 land -- with a matrix phase
+  // M(c+1) -- S^T tiles of chunk c+1 and O^T += V^T P^T of chunk c.  Group 1
+  // passes one extra barrier first, so it runs V(c) while group 0 runs
+  // M(c+1) and M(c+1) while group 0 runs V(c+1): each SIMD's matrix core
+  // works for one wavefront while the other computes exponentials.
+  const int grp = w >> 2;
+  const int ncomp = wnp > 0 ? min(nchunks, (wlast - it.k0) / 32 + 1) : 0;
+  u32x4 kop[8], vop[8];
+  f32x4 sc[NT][2];
+  u32x4 pb[NT];
+  bool first_pass = true;
+
+  auto phase_m = [&](int c) {
+    const bool do_qk = c >= 0 && c < ncomp;
+    const bool do_pv = c >= 1 && c - 1 < ncomp;
+    if (!do_qk && !do_pv) return;
+    __builtin_amdgcn_s_setprio(1);
+    // the V^T operands of chunk c-1 land while the S^T tiles are computed
+    if (do_pv) {
+      lds_read_v(lds_lane_addr(slot(c - 1), lane), vop);
+      wait_lds_but8_for(kop);
+    } else {
+      wait_lds_for(kop);
     }
-    // causal masking is needed only where a key can lie past a column's
-    // position (or past the tile, or on empty columns)
-    const bool masked = key0 + 31 > wpos0 || wnp < WP || key0 + 32 > it.k1;
-    // phase 1: all S^T tiles, eight independent accumulation chains
-    f32x4 sc[NT][2];
+    if (do_qk) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        sc[nt][0] = mfma(kop[c], qb[nt][c], sc[nt][0]);
-        sc[nt][1] = mfma(kop[4 + c], qb[nt][c], sc[nt][1]);
+        for (int nt = 0; nt < NT; ++nt) {
+          sc[nt][0] = mfma(kop[k], qb[nt][k], sc[nt][0]);
+          sc[nt][1] = mfma(kop[4 + k], qb[nt][k], sc[nt][1]);
+        }
+    }
+    if (do_pv) {
+      wait_lds_for(vop);
+      const int key0 = it.k0 + 32 * (c - 1);
+      if (key0 + 32 > it.k1) {
+        // keys past the tile may hold stale data: zero their values
+        const int nv = it.k1 - (key0 + 8 * g);
+        u32x4 keep;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
       }
-    // the V^T operands land while the softmax runs
-    lds_read_v(laddr, vop);
-    // phase 2: masking and per-lane maxima of every column tile
-    float sv[NT][8], mx[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(vop[dt], pb[nt], acc[nt][dt]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto phase_v = [&](int c) {
+    // reads for the next matrix phase first, so they land during the softmax
+    if (c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(c + 1), lane), kop);
+    if (c < 0 || c >= ncomp) return;
+    const int key0 = it.k0 + 32 * c;
+    const int kl = key0 + 8 * g;
+    float sv[NT][8];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sv[nt][i] = sc[nt][0][i];
         sv[nt][4 + i] = sc[nt][1][i];
       }
-      if (masked) {
+    // causal masking is needed only where a key can lie past a column's
+    // position (or past the tile, or on empty columns)
+    if (key0 + 31 > wpos0 || wnp < WP || key0 + 32 > it.k1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = kl + j;
           sv[nt][j] = (col_ok[nt] && key < it.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
         }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      m_hi[nt] = max3(max3(max3(m_hi[nt], sv[nt][0], sv[nt][1]), max3(sv[nt][2], sv[nt][3], sv[nt][4]),
+                           sv[nt][5]),
+                      sv[nt][6], sv[nt][7]);
+    if (c == 0 && first_pass) {
+      // the reference: the column's maximum over the first chunk
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mx = xmax32(xmax16(m_hi[nt]));
+        neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
       }
-      mx[nt] = sv[nt][0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) mx[nt] = fmaxf(mx[nt], sv[nt][j]);
-    }
-    // phase 3: column maxima across the four lane groups
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax16(mx[nt]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) mx[nt] = xmax32(mx[nt]);
-    // phase 4: probabilities in bf16 against the column's reference
-    u32x4 pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mxs = mx[nt] == neg_inf() ? neg_inf() : mx[nt] * c2;
-      if (m_ref[nt] == neg_inf()) m_ref[nt] = mxs;
-      m_hi[nt] = fmaxf(m_hi[nt], mxs);
-      const float m_use = m_ref[nt] == neg_inf() ? 0.f : m_ref[nt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pb[nt][i] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i], c2, -m_use)),
-                              __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i + 1], c2, -m_use)));
-    }
-    // phase 5: O^T += V^T P^T and the column sums
-    wait_lds();
-    if (vz) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vop[i] = u32x4{0, 0, 0, 0};
-    }
-    if (key0 + 32 > it.k1) {
-      // keys past the tile may hold stale data: zero their values
-      const int nv = it.k1 - kl;
-      u32x4 keep;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(vop[dt], pb[nt], acc[nt][dt]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lacc[nt] = mfma(ones, pb[nt], lacc[nt]);
+      for (int i = 0; i < 4; ++i) {
+        pb[nt][i] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i], c2, neg_ref[nt])),
+                              __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i + 1], c2, neg_ref[nt])));
+        l_part[nt] = sum_bf16x2(pb[nt][i], l_part[nt]);
+      }
   };
 
-  // One step: chunk cc's loads complete (the next chunk's may still fly),
-  // barrier, refill the buffer freed by chunk cc-1 with chunk cc+2, compute.
-  // f0 / f1 / f2: out-of-range flags of chunks cc, cc+1, cc+2.
-  const int ncomp = wnp > 0 ? min(nchunks, (wlast - it.k0) / 32 + 1) : 0;
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      // second pass: the exact maximum of the first is the reference
-      m_ref[nt] = pass == 0 ? neg_inf() : m_hi[nt];
-      if (pass == 0) m_hi[nt] = neg_inf();
-      lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_part[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (pass == 0) {
+        m_hi[nt] = neg_inf();
+        neg_ref[nt] = 0.f;
+      }
     }
     if (pass == 0) {
       if (w == 0 && lane == 0) lds_restart = 0;
       __syncthreads();
     }
-    int f0 = issue(0, lds_chunks), f1 = 0;
-    if (nchunks > 1) f1 = issue(1, lds_chunks + kChunkVec);
-    int cur = 0;  // buffer of chunk cc
-    auto advance = [&](int cc) -> int {  // wait, barrier, refill; returns chunk cc+2's flags
-      if (cc + 1 < nchunks)
-        wait_vmcnt<RPW>();
-      else
-        wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      const int refill = cur == 0 ? 2 : cur - 1;  // (cc + 2) % 3
-      return cc + 2 < nchunks ? issue(cc + 2, lds_chunks + refill * kChunkVec) : 0;
-    };
-    // chunks holding keys at or before this wavefront's last position are
-    // computed; later ones only keep the workgroup's loads and barriers going
-    int cc = 0;
-    for (; cc < ncomp; ++cc) {
-      const int f2 = advance(cc);
-      compute(cc, lds_chunks + cur * kChunkVec, f0);
-      f0 = f1;
-      f1 = f2;
-      cur = cur == 2 ? 0 : cur + 1;
+    // Chunk c lives in slot c % kNbuf from the barrier before group 0's
+    // V(c-1) (which reads its K) to group 1's M(c+1) (which reads its V^T);
+    // three steps after its first use the slot takes chunk c + kNbuf.
+    // Group 0 loads the K regions and group 1, half a step later, the V^T
+    // regions, which are first read a step after the K regions of the chunk.
+    for (int c = 0; c < kAhead && c < nchunks; ++c) issue(c);
+    if (grp == 1) barrier();
+    for (int s = 0; s <= nchunks; ++s) {
+      // every LDS read of this wavefront is done (its slot may be refilled)
+      // and its loads of chunk s have landed; chunks s+1 .. s+kAhead-1 may fly
+      wait_lds();
+      switch (min(nchunks - 1 - s, kAhead - 1)) {
+        case 4: wait_vmcnt<4 * RPW>(); break;
+        case 3: wait_vmcnt<3 * RPW>(); break;
+        case 2: wait_vmcnt<2 * RPW>(); break;
+        case 1: wait_vmcnt<RPW>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+      barrier();
+      if (s + kAhead < nchunks) issue(s + kAhead);
+      phase_v(s - 1);
+      barrier();
+      phase_m(s);
     }
-    for (; cc < nchunks; ++cc) {
-      advance(cc);
-      cur = cur == 2 ? 0 : cur + 1;
-    }
+    if (grp == 0) barrier();
     if (pass == 1) break;
     // did any column of any wavefront outgrow its reference by 2^100?
     bool grew = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) grew |= m_hi[nt] > m_ref[nt] + 100.f;
+    for (int nt = 0; nt < NT; ++nt) grew |= __builtin_fmaf(m_hi[nt], c2, neg_ref[nt]) > 100.f;
     if (__builtin_amdgcn_ballot_w64(grew) && lane == 0) atomicOr(&lds_restart, 1);
     __syncthreads();
     const bool again = lds_restart != 0;
     __syncthreads();
     if (!again) break;
+    // second pass: the exact maximum of the first is the reference
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = xmax32(xmax16(m_hi[nt]));
+      neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
+    }
+    first_pass = false;
   }
 
-  // epilogue: column sums sit in row 0 (lanes 0..15, element 0)
+  // epilogue: column sums over the four lane groups, then O / l
+  float l_tot[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float l_tot = __shfl(lacc[nt][0], r);
     if (!col_ok[nt]) continue;
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / l_tot[nt];
     uint16_t *op = a.out + col_qoff[nt] + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -810,6 +863,8 @@ int check_plan(const pkv_plan_t *plan, size_t ws_bytes, const void *ws) {
   if (plan->head_dim != D || plan->num_q_heads <= 0 || plan->num_kv_heads <= 0) return PKV_EINVAL;
   if (plan->num_items > 0 && !ws) return PKV_EINVAL;
   if (ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
+  if (plan->zero_off < 0 || (size_t)plan->zero_off + (size_t)pkv::kBlock * D * 2 > plan->ws_bytes)
+    return PKV_EINVAL;
   return PKV_OK;
 }
 
@@ -832,7 +887,7 @@ const char *pkv_status_string(int status) {
   }
 }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 101; }
 
 int pkv_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                      const int32_t *block_tables, int32_t bt_stride, int32_t num_seqs,
@@ -876,6 +931,8 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   if (plan->num_items == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !out || bt_stride <= 0 || num_blocks <= 0)
     return PKV_EINVAL;
+  // (block, kv head) tiles are indexed in 32 bits
+  if (num_blocks > (int64_t)UINT32_MAX / plan->num_kv_heads) return PKV_ERANGE;
   const int G = plan->num_q_heads / plan->num_kv_heads;
   AttnArgs a;
   a.q = q;
@@ -888,6 +945,7 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.waves = reinterpret_cast<const int32_t *>(w + plan->waves_off);
   a.part_ml = reinterpret_cast<float2 *>(w + plan->ml_off);
   a.part_o = reinterpret_cast<float *>(w + plan->o_off);
+  a.zero = reinterpret_cast<const uint16_t *>(w + plan->zero_off);
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
   a.num_items = plan->num_items;

@@ -203,13 +203,17 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   const size_t items_b = pkv::align_up(items.size() * sizeof(Item));
   const size_t waves_b = pkv::align_up(wave_off.size() * sizeof(int32_t));
   const size_t merge_b = pkv::align_up(merges.size() * sizeof(Merge));
+  // a zero (block, head) tile: loads of table entries outside [0, num_blocks)
+  // are pointed at it
+  const size_t zero_b = (size_t)pkv::kBlock * pkv::kHeadDim * 2;
   plan->items_off = 0;
   plan->waves_off = (int64_t)items_b;
   plan->merge_off = (int64_t)(items_b + waves_b);
-  plan->ml_off = (int64_t)(items_b + waves_b + merge_b);
+  plan->zero_off = (int64_t)(items_b + waves_b + merge_b);
+  plan->ml_off = plan->zero_off + (int64_t)zero_b;
   plan->o_off = plan->ml_off + (int64_t)pkv::align_up((size_t)part_cols * 8);
   plan->ws_bytes = (size_t)plan->o_off + (size_t)part_cols * pkv::kHeadDim * 4;
-  plan->host_bytes = items_b + waves_b + merge_b;
+  plan->host_bytes = items_b + waves_b + merge_b + zero_b;
   if (!h_staging) return PKV_OK;  // size query
   if (h_staging_bytes < plan->host_bytes) return PKV_EWORKSPACE;
   if (ws && ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
@@ -218,6 +222,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   if (!items.empty()) std::memcpy(hs, items.data(), items.size() * sizeof(Item));
   if (!wave_off.empty()) std::memcpy(hs + items_b, wave_off.data(), wave_off.size() * sizeof(int32_t));
   if (!merges.empty()) std::memcpy(hs + items_b + waves_b, merges.data(), merges.size() * sizeof(Merge));
+  std::memset(hs + plan->zero_off, 0, zero_b);
   if (ws && plan->host_bytes > 0) {
     hipError_t e = hipMemcpyAsync(ws, h_staging, plan->host_bytes, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));
