@@ -1,17 +1,20 @@
 // HIP kernels for one packed, ragged attention step over a paged KV cache,
 // written for CDNA4 (gfx950, wave64, bf16 MFMA).
 //
-//   slot_mapping_kernel  slot translation b*16 + p%16
-//                        ("连续批处理与 PagedAttention 原理", "block table 与地址映射")
-//   kv_append_kernel     bit copy of the step's new K/V rows into their slots
-//   attention_kernel     fused decode + prefill tiles over the plan's items
-//   merge_kernel         log-sum-exp merge of key-split partial results
+//   slot_mapping_kernel     slot translation b*16 + p%16
+//                           ("连续批处理与 PagedAttention 原理", "block table 与地址映射")
+//   append_kernel           bit copy of the step's new K/V rows into their slots
+//                           (optionally translating the slots first)
+//   attention_kernel        narrow items only (decode rows, short tiles)
+//   attention_mixed_kernel  wide prefill tiles (eight-wavefront workgroups
+//                           sharing K/V through LDS) and narrow items in one grid
+//   merge_kernel            log-sum-exp merge of key-split partial results
 //
-// Attention, per item (one wavefront): a tile of query columns (positions x
-// the GQA group's query heads, all reading the same kv head) against a key
-// range of one sequence, 32 keys (two paged blocks) per step:
+// Attention: a tile of query columns (positions x the GQA group's query
+// heads, all reading the same kv head) against a key range of one sequence,
+// 32 keys (two paged blocks) per step:
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, M = keys, N = columns, K = dims)
-//   online softmax per column in the base-2 domain, fp32
+//   softmax per column in the base-2 domain, fp32
 //   O^T += V^T P^T (same MFMA, M = dims, N = columns, K = keys)
 // Operand layouts of the 16x16x32 MFMA (lane l, r = l % 16, g = l / 16):
 //   A[m][k]: lane holds A[r][8g .. 8g+7];  B[k][n]: lane holds B[8g .. 8g+7][r]
@@ -21,8 +24,9 @@
 // as the B operand (P^T) of the P.V product.  The V tile of a block is
 // stored dimension-major (16 tokens contiguous per dimension), so the V^T A
 // operand is one 16-byte load per lane; K tiles are token-major and the K A
-// operand is one 16-byte load per lane per 32 dimensions.  No LDS, no
-// transposes: every operand comes straight from HBM in its MFMA layout.
+// operand is one 16-byte load per lane per 32 dimensions.  Narrow items load
+// their operands straight from HBM in MFMA layout; wide tiles stage each
+// chunk once per workgroup in LDS, in the same layout.
 #include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
@@ -129,54 +133,64 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// append: one thread per (row, kv head, 8 dimensions)
+// append: a workgroup per 16 consecutive packed rows and one kv head, a
+// thread per (row, 8 dimensions) for K and for V.  K rows are token-major in
+// the cache: lanes run over dimensions, each row's 256 bytes are one
+// contiguous store.  V tiles are dimension-major (a block's 16 tokens
+// contiguous per dimension): lanes run over rows, so each 2-byte store
+// instruction writes, per dimension, the consecutive slots of up to 16
+// consecutive rows -- whole sectors inside any prefill run, whatever its
+// alignment; decode rows touch one slot of a block each.
 // ---------------------------------------------------------------------------
-__device__ inline void append_one(const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-                                  int t, int h, int d0, int Hkv, int64_t slot, uint16_t *__restrict__ kc,
-                                  uint16_t *__restrict__ vc) {
-  const int64_t b = slot >> 4;
-  const int o = (int)(slot & 15);
-  const int64_t src = ((int64_t)t * Hkv + h) * D + d0;
-  const int64_t tile = (b * Hkv + h) * TILE;
-  *reinterpret_cast<u32x4 *>(kc + tile + o * D + d0) = load16(k_new + src);
-  const u32x4 v = load16(v_new + src);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    vc[tile + (d0 + 2 * i) * pkv::kBlock + o] = (uint16_t)(v[i] & 0xFFFF);
-    vc[tile + (d0 + 2 * i + 1) * pkv::kBlock + o] = (uint16_t)(v[i] >> 16);
-  }
-}
+constexpr int kAppendRows = 16;
 
-__global__ __launch_bounds__(256) void kv_append_kernel(
+__global__ __launch_bounds__(256) void append_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
-    const int64_t *__restrict__ slots, int32_t T, int32_t Hkv, int64_t num_blocks,
-    uint16_t *__restrict__ kc, uint16_t *__restrict__ vc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)Hkv * (D / 8);
-  if (idx >= (int64_t)T * per_row) return;
-  const int t = (int)(idx / per_row);
-  const int rem = (int)(idx - (int64_t)t * per_row);
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_blocks * pkv::kBlock) return;
-  append_one(k_new, v_new, t, rem / (D / 8), (rem % (D / 8)) * 8, Hkv, slot, kc, vc);
-}
-
-// slot translation and append in one launch (the whole-step entry point)
-__global__ __launch_bounds__(256) void slot_append_kernel(
-    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    const int64_t *__restrict__ slot_in,  // given slots, or null: translate
     const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
-    int64_t num_blocks, int64_t *__restrict__ slots, uint16_t *__restrict__ kc,
+    int64_t num_blocks, int64_t *__restrict__ slot_out, uint16_t *__restrict__ kc,
     uint16_t *__restrict__ vc) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)Hkv * (D / 8);
-  if (idx >= (int64_t)T * per_row) return;
-  const int t = (int)(idx / per_row);
-  const int rem = (int)(idx - (int64_t)t * per_row);
-  const int64_t slot = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
-  if (rem == 0) slots[t] = slot;
-  if (slot < 0) return;
-  append_one(k_new, v_new, t, rem / (D / 8), (rem % (D / 8)) * 8, Hkv, slot, kc, vc);
+  __shared__ int64_t srow[kAppendRows];
+  const int t0 = blockIdx.x * kAppendRows;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < kAppendRows) {
+    const int t = t0 + tid;
+    int64_t sl = -1;
+    if (t < T) {
+      if (slot_in) {
+        sl = slot_in[t];
+        if (sl < 0 || sl >= num_blocks * pkv::kBlock) sl = -1;
+      } else {
+        sl = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
+        if (h == 0) slot_out[t] = sl;
+      }
+    }
+    srow[tid] = sl;
+  }
+  __syncthreads();
+  {  // K: lanes over dimensions
+    const int i = tid >> 4, d0 = 8 * (tid & 15);
+    const int64_t sl = srow[i];
+    if (t0 + i < T && sl >= 0) {
+      const u32x4 x = load16(k_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
+      *reinterpret_cast<u32x4 *>(kc + ((sl >> 4) * Hkv + h) * TILE + (sl & 15) * D + d0) = x;
+    }
+  }
+  {  // V: lanes over rows
+    const int i = tid & 15, d0 = 8 * (tid >> 4);
+    const int64_t sl = srow[i];
+    if (t0 + i < T && sl >= 0) {
+      const u32x4 x = load16(v_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
+      uint16_t *dst = vc + ((sl >> 4) * Hkv + h) * TILE + (int64_t)d0 * pkv::kBlock + (sl & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[(2 * e) * pkv::kBlock] = (uint16_t)(x[e] & 0xFFFF);
+        dst[(2 * e + 1) * pkv::kBlock] = (uint16_t)(x[e] >> 16);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -912,12 +926,10 @@ int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
   if (head_dim != D) return PKV_EUNSUPPORTED;
   if (num_rows == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
-  const int64_t total = (int64_t)num_rows * num_kv_heads * (D / 8);
-  const int64_t grid = (total + 255) / 256;
-  if (grid > INT32_MAX) return PKV_ERANGE;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
-                     k_new, v_new, slot_mapping, num_rows, num_kv_heads, num_blocks, k_cache,
-                     v_cache);
+  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, num_kv_heads);
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, slot_mapping,
+                     nullptr, nullptr, nullptr, 0, 0, num_rows, num_kv_heads, num_blocks, nullptr,
+                     k_cache, v_cache);
   return launch_status();
 }
 
@@ -1002,12 +1014,10 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t 
   if (!k_new || !v_new || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables ||
       !slot_mapping || num_seqs == 0)
     return PKV_EINVAL;
-  const int64_t total = (int64_t)num_rows * num_kv_heads * (D / 8);
-  const int64_t grid = (total + 255) / 256;
-  if (grid > INT32_MAX) return PKV_ERANGE;
-  hipLaunchKernelGGL(slot_append_kernel, dim3((unsigned)grid), dim3(256), 0, as_stream(stream),
-                     k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs,
-                     num_rows, num_kv_heads, num_blocks, slot_mapping, k_cache, v_cache);
+  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, num_kv_heads);
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, nullptr,
+                     cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs, num_rows, num_kv_heads,
+                     num_blocks, slot_mapping, k_cache, v_cache);
   return launch_status();
 }
 
