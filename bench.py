@@ -38,6 +38,7 @@ WORKLOADS = {
     "longshared": "config_long_shared",
     "prefillchunk": "config_prefill_chunk",
     "prefillfresh": "config_prefill_fresh",
+    "tracestep": "config_trace_step",
 }
 
 

@@ -154,7 +154,9 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * ------------------------------------------------------------------------- */
 typedef struct pkv_plan_options {
   int32_t narrow_waves;   /* wavefronts sharing the decode work (0 = default:
-                             1024, or 2048 when the plan has wide tiles) */
+                             1024; with wide tiles, 64 per row of narrow
+                             workgroups, rows sized to the estimated share of
+                             the narrow work; at most 2048 with wide tiles) */
   int32_t min_wave_keys;  /* smallest share per wavefront, keys (0 = default) */
   int32_t wide_tiles;     /* -1 auto, 0 never, 1 always use wide prefill tiles */
   int32_t reserved;
@@ -168,7 +170,8 @@ typedef struct pkv_plan {
   int32_t num_merge;      /* merge entries (one per split output row x head) */
   int32_t num_part_cols;  /* partial-result columns in the workspace */
   int32_t wave_keys;      /* keys per wavefront share */
-  int32_t reserved;
+  int32_t narrow_rows;    /* mixed launch: rows of eight workgroups (at most 32)
+                             carrying the narrow wavefronts */
   int64_t items_off, waves_off, merge_off, ml_off, o_off; /* byte offsets into ws */
   int64_t zero_off;       /* byte offset of a 4 KiB all-zero tile in ws */
   size_t ws_bytes;        /* workspace bytes this plan uses */

@@ -47,7 +47,7 @@ class PlanStruct(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("num_items", ctypes.c_int32),
                 ("num_wide_items", ctypes.c_int32), ("num_waves", ctypes.c_int32),
                 ("num_merge", ctypes.c_int32), ("num_part_cols", ctypes.c_int32),
-                ("wave_keys", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("wave_keys", ctypes.c_int32), ("narrow_rows", ctypes.c_int32),
                 ("items_off", ctypes.c_int64), ("waves_off", ctypes.c_int64),
                 ("merge_off", ctypes.c_int64), ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
                 ("zero_off", ctypes.c_int64),

@@ -29,6 +29,8 @@
 // chunk once per workgroup in LDS, in the same layout.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pkv_internal.h"
 
 namespace {
@@ -207,6 +209,7 @@ struct AttnArgs {
   float2 *part_ml;
   float *part_o;
   const uint16_t *zero;  // one all-zero (block, head) tile
+  int32_t narrow_rows;   // mixed launch: rows of eight workgroups carrying narrow shares
   int64_t num_blocks;
   int32_t bt_stride;
   int32_t num_items;
@@ -816,17 +819,41 @@ void attention_kernel(AttnArgs a) {
   }
 }
 
-// Mixed launch: workgroups [0, num_wide) run wide prefill tiles (eight
-// wavefronts sharing K/V through LDS); the rest carry eight narrow
-// wavefronts each, walking their item shares.
+// Mixed launch.  Workgroups come in rows of eight (consecutive workgroups
+// go to the eight XCDs in turn).  narrow_rows rows, spread evenly over the
+// first 32 rows (the workgroups that start at once, one per CU), carry eight
+// narrow wavefronts each, walking their item shares; every other row holds
+// eight wide tiles in item order (longest first), so wide item i runs on
+// XCD i % 8 and the tiles of a kv head share an L2.  The bandwidth-bound
+// narrow shares thus stream on some CUs while the others work through the
+// matrix-bound wide tiles, and a CU whose narrow workgroup ends takes the
+// next wide tile.
+__device__ __forceinline__ void mixed_row(int rows, int narrow_rows, int rho, bool &narrow, int &ord) {
+  const int S = min(32, rows);  // rows started at once
+  if (rho < S) {
+    const int lo = rho * narrow_rows / S, hi = (rho + 1) * narrow_rows / S;
+    narrow = hi > lo;
+    ord = narrow ? lo : rho - lo;
+  } else {
+    narrow = false;
+    ord = rho - narrow_rows;
+  }
+}
+
 __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(AttnArgs a) {
-  const int b = blockIdx.x;
-  if (b < a.num_wide) {
-    const Item it = load_item(a, b);
+  static_assert(pkv::kWideWaves == 8, "rows of eight workgroups of eight wavefronts");
+  const int rows = a.narrow_rows + (a.num_wide + 7) / 8;
+  bool narrow;
+  int ord;
+  mixed_row(rows, a.narrow_rows, blockIdx.x / 8, narrow, ord);
+  const int wg = ord * 8 + blockIdx.x % 8;
+  if (!narrow) {
+    if (wg >= a.num_wide) return;
+    const Item it = load_item(a, wg);
     if (it.k1 > it.k0 && it.np > 0) run_wide_tile(a, it);
     return;
   }
-  const int w = (b - a.num_wide) * pkv::kWideWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wg * 8 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (w >= a.num_waves) return;
   const int i0 = a.num_wide + sload(a.waves, w);
   const int i1 = a.num_wide + sload(a.waves, w + 1);
@@ -958,6 +985,7 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.part_ml = reinterpret_cast<float2 *>(w + plan->ml_off);
   a.part_o = reinterpret_cast<float *>(w + plan->o_off);
   a.zero = reinterpret_cast<const uint16_t *>(w + plan->zero_off);
+  a.narrow_rows = plan->narrow_rows;
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
   a.num_items = plan->num_items;
@@ -968,11 +996,13 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.log2G = pkv::log2_exact(G);
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
-  if (plan->num_wide_items > 0)
-    hipLaunchKernelGGL(attention_mixed_kernel,
-                       dim3(plan->num_wide_items + (plan->num_waves + pkv::kWideWaves - 1) / pkv::kWideWaves),
-                       dim3(64 * pkv::kWideWaves), 0, as_stream(stream), a);
-  else if (plan->num_waves > 0)
+  if (plan->num_wide_items > 0) {
+    if (plan->narrow_rows < 0 || plan->narrow_rows > 32 || (int64_t)plan->narrow_rows * 64 < plan->num_waves)
+      return PKV_EINVAL;
+    const int64_t rows = plan->narrow_rows + ((int64_t)plan->num_wide_items + 7) / 8;
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3((unsigned)(rows * 8)), dim3(64 * pkv::kWideWaves), 0,
+                       as_stream(stream), a);
+  } else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();
 }

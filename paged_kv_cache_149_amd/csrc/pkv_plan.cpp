@@ -28,11 +28,7 @@ namespace {
 using pkv::Item;
 using pkv::Merge;
 
-// Narrow wavefronts: one per SIMD on 256 CUs for a narrow-only launch; in a
-// mixed launch they travel eight to a workgroup, so twice as many keep every
-// CU streaming while the wide tiles occupy some of them.
-constexpr int kDefaultNarrowWaves = 1024;
-constexpr int kDefaultNarrowWavesMixed = 2048;
+constexpr int kDefaultNarrowWaves = 1024;  // one per SIMD on 256 CUs
 constexpr int kDefaultMinWaveKeys = 512;
 
 int round_up32(int64_t x) { return (int)((x + 31) / 32 * 32); }
@@ -116,20 +112,36 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   for (const Tile &t : wide_tiles)
     for (int h = 0; h < Hkv; ++h) items.push_back(Item{t.seq, h, t.t0, t.np, t.pos0, 0, t.keys, -1});
   const int n_wide = (int)items.size();
-  const int want_waves = (opts && opts->narrow_waves > 0) ? opts->narrow_waves
-                         : n_wide > 0                    ? kDefaultNarrowWavesMixed
-                                                         : kDefaultNarrowWaves;
 
   // narrow units (tile, kv head) in order; chunk counts
   const int64_t n_units = (int64_t)narrow_tiles.size() * Hkv;
   int64_t total_chunks = 0;
   for (const Tile &t : narrow_tiles) total_chunks += (int64_t)Hkv * ((t.keys + 31) / 32);
+
+  // Narrow wavefronts.  Alone they are one per SIMD.  In a mixed launch they
+  // travel in rows of eight workgroups of eight, started beside the wide
+  // tiles; the rows get the share of the chip the narrow work is estimated
+  // to need: wide tiles at ~1 PFLOP/s, narrow 32-key chunks (K and V of one
+  // kv head, 16 KiB) at ~6 TB/s.
+  int narrow_rows = 0;
+  int want_waves = kDefaultNarrowWaves;
+  if (n_wide > 0 && total_chunks > 0) {
+    double wide_flop = 0;
+    for (int i = 0; i < n_wide; ++i)
+      wide_flop += 4.0 * head_dim * G * (double)items[i].np * (items[i].k1 - items[i].k0);
+    const double tw = wide_flop / 1.0e15, tn = (double)total_chunks * 32 * 4 * head_dim / 6.0e12;
+    narrow_rows = std::max(1, std::min(32, (int)(32.0 * tn / (tw + tn) + 0.5)));
+    want_waves = 64 * narrow_rows;
+  }
+  if (opts && opts->narrow_waves > 0) want_waves = opts->narrow_waves;
+  if (n_wide > 0) want_waves = std::min(want_waves, 64 * 32);
   int W = 0;
   int wave_keys = 0;
   if (total_chunks > 0) {
     const int64_t by_size = (total_chunks * 32 + min_wave_keys - 1) / min_wave_keys;
     W = (int)std::max<int64_t>(1, std::min<int64_t>(want_waves, by_size));
     wave_keys = (int)((total_chunks + W - 1) / W * 32);
+    if (n_wide > 0) narrow_rows = (W + 63) / 64;
   }
   auto unit_tile = [&](int64_t u) -> const Tile & { return narrow_tiles[u / Hkv]; };
   auto unit_chunks = [&](int64_t u) -> int { return (unit_tile(u).keys + 31) / 32; };
@@ -194,6 +206,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   plan->head_dim = head_dim;
   plan->num_items = (int32_t)items.size();
   plan->num_wide_items = n_wide;
+  plan->narrow_rows = narrow_rows;
   plan->num_waves = W;
   plan->num_merge = (int32_t)merges.size();
   plan->num_part_cols = (int32_t)part_cols;

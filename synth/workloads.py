@@ -365,3 +365,14 @@ def config_prefill_fresh(seed: int = 149007, n: int = 4, length: int = 2048, **k
     """Prefill-heavy: four 2048-token prompts with nothing cached (an 8192-token
     budget of fresh prefill)."""
     return make_batch(f"prefill-{n}x{length}-fresh", [(0, length)] * n, seed=seed, **kw)
+
+
+def config_trace_step(index: int = 150, seed: int = 149008, **kw) -> Batch:
+    """One step of the continuous-batching trace (default step 150: about 735
+    decode rows beside ~7,460 rows of prefill chunks), with fresh N(0,1)
+    values for its rows and every pool tile it references."""
+    from synth import scheduler as sc
+    steps, sch = sc.continuous_batching_trace(sc.TraceConfig(steps=index + 1))
+    st = steps[index]
+    return batch_from_metadata(f"trace-step{index}-{st.num_rows}rows-{st.n_decode}decode", st.cu_seqlens_q,
+                               st.seq_lens, st.block_tables, sch.pool.num_blocks, seed=seed, **kw)
