@@ -202,7 +202,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": measured_traffic(args.workload), "kernel": "attention_kernel", "avg_ms": round(attn_ms, 5),
+    kernel = "attention_mixed_kernel" if plan.num_wide_items > 0 else "attention_kernel"
+    roof.update({"traffic": measured_traffic(args.workload), "kernel": kernel, "avg_ms": round(attn_ms, 5),
                  "bytes_per_launch": nbytes["total"], "flop_per_launch": flop})
 
     cpu = None
