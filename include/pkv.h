@@ -131,7 +131,11 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * chunked prefill, whose causal offset is the cached prefix: "Continuous
  * Batching 深入实现", section "一个 chunked prefill 请求怎么组织 attention")
  * become tiles of query positions x the kv head's query heads; a wide tile
- * (256 columns: up to 256/G positions) is one workgroup's item.  Everything else -- decode rows and
+ * (256 columns: up to 256/G positions) is computed by one whole workgroup.
+ * The launch has a fixed set of persistent workgroups (rows of eight, one
+ * per CU); each walks a list of wide tiles that the plan deals out longest
+ * first to the least loaded workgroup, tiles of kv head h to the workgroups
+ * of XCD h % 8 when Hkv is a multiple of 8.  Everything else -- decode rows and
  * short tiles ("11.2 连续批处理与 PagedAttention", section 11.2.2: attention
  * runs per request inside one launch) -- is a (tile, kv head) unit whose
  * keys stream through the cache; all units' 32-key chunks are dealt out in
@@ -159,25 +163,33 @@ typedef struct pkv_plan_options {
                              the narrow work; at most 2048 with wide tiles) */
   int32_t min_wave_keys;  /* smallest share per wavefront, keys (0 = default) */
   int32_t wide_tiles;     /* -1 auto, 0 never, 1 always use wide prefill tiles */
-  int32_t reserved;
+  int32_t workgroups;     /* persistent workgroups of a launch with wide tiles
+                             (0 = default: 256, one per CU of an MI355X; a
+                             multiple of 8, at most 256) */
 } pkv_plan_options_t;
 
 typedef struct pkv_plan {
   int32_t num_seqs, num_rows, num_q_heads, num_kv_heads, head_dim;
   int32_t num_items;      /* attention work items */
-  int32_t num_wide_items; /* wide tiles: items [0, num_wide_items), one per workgroup */
+  int32_t num_wide_items; /* wide tiles: items [0, num_wide_items), grouped by workgroup */
   int32_t num_waves;      /* wavefronts walking the remaining items */
   int32_t num_merge;      /* merge entries (one per split output row x head) */
   int32_t num_part_cols;  /* partial-result columns in the workspace */
   int32_t wave_keys;      /* keys per wavefront share */
-  int32_t narrow_rows;    /* mixed launch: rows of eight workgroups (at most 32)
-                             carrying the narrow wavefronts */
+  int32_t narrow_rows;    /* launch with wide tiles: rows of eight workgroups
+                             (at most 32) whose wavefronts first walk the
+                             narrow shares */
   int64_t items_off, waves_off, merge_off, ml_off, o_off; /* byte offsets into ws */
   int64_t zero_off;       /* byte offset of a 4 KiB all-zero tile in ws */
   size_t ws_bytes;        /* workspace bytes this plan uses */
   size_t host_bytes;      /* host staging bytes this plan uses */
   int64_t kv_keys;        /* sum over sequences of visible keys (accounting) */
   int64_t visible_pairs;  /* sum over rows of visible keys (accounting) */
+  int32_t num_workgroups; /* workgroups of a launch with wide tiles (0 if none) */
+  int32_t reserved;
+  int64_t wg_off;         /* byte offset in ws of int32[num_workgroups + 1]:
+                             workgroup j's wide tiles are items
+                             [list[j], list[j + 1]) */
 } pkv_plan_t;
 
 int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,

@@ -38,7 +38,7 @@ class PKVError(RuntimeError):
 
 class PlanOptions(ctypes.Structure):
     _fields_ = [("narrow_waves", ctypes.c_int32), ("min_wave_keys", ctypes.c_int32),
-                ("wide_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("wide_tiles", ctypes.c_int32), ("workgroups", ctypes.c_int32)]
 
 
 class PlanStruct(ctypes.Structure):
@@ -52,7 +52,9 @@ class PlanStruct(ctypes.Structure):
                 ("merge_off", ctypes.c_int64), ("ml_off", ctypes.c_int64), ("o_off", ctypes.c_int64),
                 ("zero_off", ctypes.c_int64),
                 ("ws_bytes", ctypes.c_size_t), ("host_bytes", ctypes.c_size_t),
-                ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64)]
+                ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64),
+                ("num_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("wg_off", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -228,6 +230,13 @@ class Plan:
         relative to item num_wide_items)."""
         n = self.st.num_waves + 1
         off = self.st.waves_off
+        return self.staging[off:off + n * 4].numpy().view(np.int32).copy()
+
+    def wg_lists(self) -> np.ndarray:
+        """Item offsets of the persistent workgroups' wide-tile lists
+        (num_workgroups + 1 entries)."""
+        n = self.st.num_workgroups + 1 if self.st.num_workgroups > 0 else 0
+        off = self.st.wg_off
         return self.staging[off:off + n * 4].numpy().view(np.int32).copy()
 
     def merges(self) -> np.ndarray:

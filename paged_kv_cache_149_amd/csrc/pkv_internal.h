@@ -40,6 +40,19 @@ static_assert(sizeof(Merge) == PKV_MERGE_INTS * 4, "merge size");
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Role of row rho (eight consecutive workgroups, one per XCD) of a launch
+// with wide tiles: narrow_rows of the rows, spread evenly over all of them,
+// first walk narrow wavefront shares (ord = their narrow row); ord of a wide
+// row counts the wide rows.  Shared by the planner and the kernel.
+struct RowRole {
+  bool narrow;
+  int ord;
+};
+constexpr RowRole mixed_row(int rows, int narrow_rows, int rho) {
+  const int lo = rho * narrow_rows / rows, hi = (rho + 1) * narrow_rows / rows;
+  return RowRole{hi > lo, hi > lo ? lo : rho - lo};
+}
+
 inline int log2_exact(int x) {
   int l = 0;
   while ((1 << l) < x) ++l;

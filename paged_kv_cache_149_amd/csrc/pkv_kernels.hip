@@ -6,8 +6,9 @@
 //   append_kernel           bit copy of the step's new K/V rows into their slots
 //                           (optionally translating the slots first)
 //   attention_kernel        narrow items only (decode rows, short tiles)
-//   attention_mixed_kernel  wide prefill tiles (eight-wavefront workgroups
-//                           sharing K/V through LDS) and narrow items in one grid
+//   attention_mixed_kernel  persistent workgroups walking lists of wide
+//                           prefill tiles (eight wavefronts sharing K/V
+//                           through LDS), some first walking narrow items
 //   merge_kernel            log-sum-exp merge of key-split partial results
 //
 // Attention: a tile of query columns (positions x the GQA group's query
@@ -209,7 +210,9 @@ struct AttnArgs {
   float2 *part_ml;
   float *part_o;
   const uint16_t *zero;  // one all-zero (block, head) tile
-  int32_t narrow_rows;   // mixed launch: rows of eight workgroups carrying narrow shares
+  const int32_t *wg_list;  // launch with wide tiles: item offsets of each workgroup's list
+  int32_t num_wg;        // launch with wide tiles: persistent workgroups
+  int32_t narrow_rows;   // launch with wide tiles: rows of eight workgroups walking narrow shares first
   int64_t num_blocks;
   int32_t bt_stride;
   int32_t num_items;
@@ -452,25 +455,26 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide prefill tile: one workgroup of eight wavefronts over one (sequence,
-// kv head) and up to 256/G query positions; wavefront w owns positions
-// [w*32/G, (w+1)*32/G) of the tile, i.e. 32 columns (positions x heads).
-// Two wavefronts share each SIMD, so one's softmax overlaps the other's
-// matrix work.  Each 32-key K/V chunk (16 KiB) is staged once per workgroup
-// in LDS with direct global->LDS loads, laid out in MFMA operand order:
-// region R (1 KiB) holds, at byte 16*l, the 16 bytes lane l needs -- K
-// operand (m-tile R/4, 32-dim step R%4) for R < 8, V^T operand (16-dim tile
-// R-8) for R >= 8.  Wavefront w loads regions 2w, 2w+1.  A ring of six
-// buffers keeps the loads of up to three chunks in flight ahead of the ones
-// being computed; two barriers per chunk pace the two wavefront groups.
+// Wide prefill tiles.  A tile covers one (sequence, kv head) and up to 256/G
+// query positions: 256 columns (positions x the group's query heads).  A
+// persistent workgroup of eight wavefronts walks a list of tiles;
+// wavefront w owns columns [32w, 32w + 32) of each, two wavefronts per
+// SIMD, so one's softmax overlaps the other's matrix work.  Keys and values
+// stream in 32-key chunks (16 KiB), each staged once per workgroup in LDS by
+// direct global->LDS loads, laid out in MFMA operand order: region R (1 KiB)
+// holds, at byte 16*l, the 16 bytes lane l needs -- K operand (m-tile R/4,
+// 32-dim step R%4) for R < 8, V^T operand (16-dim tile R-8) for R >= 8.
+// Wavefront w loads regions 2w, 2w+1 of every chunk.  The chunks of all the
+// workgroup's tiles form one stream through a ring of eight buffers that
+// keeps five chunks' loads in flight, so the next tile's first chunks land
+// while the current tile finishes.
 // ---------------------------------------------------------------------------
 constexpr int kChunkVec = 1024;  // u32x4 per chunk buffer (16 KiB)
 constexpr int kNbuf = 8;         // chunk buffers in the ring (128 KiB)
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// The ring of chunk buffers, and the workgroup's recompute flag.
+// The ring of chunk buffers.
 __shared__ __attribute__((aligned(16))) u32x4 lds_chunks[kNbuf * kChunkVec];
-__shared__ int lds_restart;
 
 // Operand regions of a staged chunk, lane `lane`'s 16 bytes each: the K
 // operands (regions 0..7) and, separately, the V^T operands (regions 8..15),
@@ -517,18 +521,55 @@ __device__ __forceinline__ void wait_lds_but8_for(u32x4 (&x)[8]) {
 #undef PKV_OPS8
 #undef PKV_DS_READ
 
+// Hands the Q^T operand registers through an empty asm statement: the
+// compiler waits for their loads here, at a fixed point after the step's
+// chunk loads, rather than wherever its loop analysis would put the wait.
+template <int NT>
+__device__ __forceinline__ void q_ready(u32x4 (&q)[NT][4]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) asm volatile("" : "+v"(q[nt][0]), "+v"(q[nt][1]), "+v"(q[nt][2]), "+v"(q[nt][3]));
+}
+
 template <int kVm>
 __device__ __forceinline__ void wait_vmcnt() {
   // s_waitcnt vmcnt(kVm), expcnt and lgkmcnt left at their maxima (no wait)
   __builtin_amdgcn_s_waitcnt((kVm & 0xF) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14));
 }
 
-__device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it) {
+// Wide tiles of the stream: wave-uniform description (keys start at 0).
+struct WideTile {
+  int32_t seq, kvh, t0, np, pos0, k1;
+  int32_t nch;     // 32-key chunks (at least one)
+  int32_t kb_end;  // one past the last block-table entry the tile reads
+};
+
+__device__ __forceinline__ WideTile wide_tile(const AttnArgs &a, int idx) {
+  const Item it = load_item(a, idx);
+  WideTile d;
+  d.seq = it.seq;
+  d.kvh = it.kvh;
+  d.t0 = it.t0;
+  d.np = it.np;
+  d.pos0 = it.pos0;
+  d.k1 = it.k1;
+  d.nch = max(1, (it.k1 + 31) >> 5);
+  d.kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
+  return d;
+}
+
+// A column's scores may exceed its reference by this much (log2 units):
+// probabilities stay below 2^100 and their sums (at most 2^31 keys) finite
+// in fp32.  A wavefront with a column past it recomputes its columns.
+constexpr float kRedoLog2 = 100.f;
+
+// The wide tiles items[i0, i1) of one persistent workgroup.
+__device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1) {
   constexpr int WV = pkv::kWideWaves;
   constexpr int NT = pkv::kWideCols / (16 * WV);  // MFMA column tiles per wavefront
   constexpr int RPW = 16 / WV;                    // operand regions loaded per wavefront
   constexpr int kAhead = kNbuf - 3;               // chunks whose loads are issued ahead
   static_assert(NT * 16 * WV == pkv::kWideCols && RPW == 2, "wide tile shape");
+  constexpr int kLoadsPerIssue = RPW;            // loads per chunk issue and wavefront
   static_assert((kNbuf & (kNbuf - 1)) == 0 && kAhead == 5, "ring of eight, waits below");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -536,51 +577,12 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
   const int r = lane & 15;
   const int G = 1 << a.log2G;
   const int WP = (pkv::kWideCols / WV) >> a.log2G;  // positions per wavefront
-  const int wpos0 = it.pos0 + w * WP;                // first position of this wavefront
-  const int wnp = max(0, min(WP, it.np - w * WP));
-  const int wlast = wpos0 + wnp - 1;                 // last position (wnp > 0)
-
-  bool col_ok[NT];
-  int col_pos[NT];
-  int64_t col_qoff[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = nt * 16 + r;
-    const int pc = col >> a.log2G;
-    const int ho = col & (G - 1);
-    col_ok[nt] = pc < wnp;
-    col_pos[nt] = wpos0 + pc;
-    col_qoff[nt] = ((int64_t)(it.t0 + w * WP + pc) * a.Hq + it.kvh * G + ho) * D;
-  }
-  u32x4 qb[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qb[nt][c] = col_ok[nt] ? load16(a.q + col_qoff[nt] + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
-
-  // Probabilities are taken relative to a fixed per-column reference: the
-  // maximum of the column's scores in the first chunk (key 0 is in it).
-  // fp32 and bf16 keep 8 exponent bits, so later scores may exceed it by
-  // up to ~2^127 without overflow and nothing is ever rescaled -- the
-  // accumulators never leave the matrix cores inside the loop.  Each lane
-  // tracks the maximum of the raw scores it sees; if any column outgrows its
-  // reference by more than 2^100, the workgroup recomputes the tile with the
-  // exact maximum from the first pass as reference (probabilities then <= 1).
-  f32x4 acc[NT][8];
-  float neg_ref[NT];  // -(reference) in log2 units
-  float m_hi[NT];     // this lane's largest raw score
-  float l_part[NT];   // this lane's sum of its rounded probabilities
-
-  const int32_t *btrow = a.bt + (int64_t)it.seq * a.bt_stride;
-  const int kb0 = it.k0 >> 4;
-  const int kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
-  const int nchunks = (it.k1 - it.k0 + 31) >> 5;
   const float c2 = a.scale_log2;
+  const uint32_t nblk = (uint32_t)a.num_blocks;
 
   // Wavefronts 0-3 load the K regions of each chunk, wavefronts 4-7 the V^T
   // regions, two each.  A lane's two regions lie in the same block of the
-  // chunk (sel) at a fixed offset (lane_off) and region distance (imm).
+  // chunk (sel) at a fixed offset (lane_off) and region distance.
   const bool kside = w < 4;
   const uint16_t *cache = kside ? a.kc : a.vc;
   int sel, lane_off;
@@ -595,212 +597,309 @@ __device__ __forceinline__ void run_wide_tile(const AttnArgs &a, const Item &it)
       lane_off = r * pkv::kBlock + 8 * (g & 1) + (R0 - 8) * 16 * pkv::kBlock;
     }
   }
-  const uint32_t nblk = (uint32_t)a.num_blocks;
-  // the (block, kv head) tile of logical block lb; table entries outside
-  // [0, num_blocks), and blocks past the item, read the all-zero tile
-  auto tile = [&](int lb) -> const uint16_t * {
-    const int b = lb < kb_end ? sload(btrow, lb) : -1;
-    return (uint32_t)b < nblk ? cache + (uint64_t)((uint32_t)b * (uint32_t)a.Hkv + (uint32_t)it.kvh) * TILE
-                              : a.zero;
-  };
   auto slot = [&](int c) -> u32x4 * { return lds_chunks + (c & (kNbuf - 1)) * kChunkVec; };
-  // this wavefront's two regions of chunk cc
-  auto issue = [&](int cc) {
-    const uint16_t *t0 = tile(kb0 + 2 * cc);
-    const uint16_t *t1 = tile(kb0 + 2 * cc + 1);
-    const uint16_t *src = (sel ? t1 : t0) + lane_off;
-    u32x4 *dst = slot(cc) + w * RPW * 64;
+
+  // ---- the chunk stream: every chunk of every tile of the list, in order,
+  // then all-zero chunks.  The cursor (tile ci, chunk ccc) issues stream
+  // chunk n_issued into ring slot n_issued % kNbuf.  Table entries outside
+  // [0, num_blocks), blocks past a tile, and the chunks after the list read
+  // the all-zero tile.  The block ids of the next issue (b0, b1) and the
+  // descriptor of the cursor's next tile (nd) are fetched one issue ahead,
+  // so no issue waits on a scalar load.  Every call issues exactly
+  // kLoadsPerIssue loads, so the loads in flight behind any chunk are known
+  // on every path.
+  int ci = i0, ccc = 0, n_issued = 0;
+  WideTile cd = wide_tile(a, i0);
+  WideTile nd = i0 + 1 < i1 ? wide_tile(a, i0 + 1) : cd;
+  int b0, b1;
+  auto fetch_ids = [&]() {
+    const int32_t *btrow = a.bt + (int64_t)cd.seq * a.bt_stride;
+    const bool live = ci < i1;
+    b0 = live && 2 * ccc < cd.kb_end ? sload(btrow, 2 * ccc) : -1;
+    b1 = live && 2 * ccc + 1 < cd.kb_end ? sload(btrow, 2 * ccc + 1) : -1;
+  };
+  fetch_ids();
+  auto issue_next = [&]() {
+    const uint32_t hoff = (uint32_t)cd.kvh;
+    auto tile = [&](int b) -> const uint16_t * {
+      return (uint32_t)b < nblk ? cache + (uint64_t)((uint32_t)b * (uint32_t)a.Hkv + hoff) * TILE : a.zero;
+    };
+    const uint16_t *src = (sel ? tile(b1) : tile(b0)) + lane_off;
+    u32x4 *dst = slot(n_issued) + w * RPW * 64;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(src + (kside ? 32 : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0, 0);
+    ++n_issued;
+    if (ci < i1 && ++ccc >= cd.nch) {
+      ccc = 0;
+      ++ci;
+      cd = nd;
+      if (ci + 1 < i1) nd = wide_tile(a, ci + 1);
+    }
+    fetch_ids();
   };
-
-  // Two groups of four wavefronts (one of each per SIMD) run half a step
-  // apart.  A wavefront alternates a vector phase V(c) -- the probabilities
-  // of chunk c, while the K operands of chunk c+1 land -- with a matrix phase
-  // M(c+1) -- S^T tiles of chunk c+1 and O^T += V^T P^T of chunk c.  Group 1
-  // passes one extra barrier first, so it runs V(c) while group 0 runs
-  // M(c+1) and M(c+1) while group 0 runs V(c+1): each SIMD's matrix core
-  // works for one wavefront while the other computes exponentials.
-  const int grp = w >> 2;
-  const int ncomp = wnp > 0 ? min(nchunks, (wlast - it.k0) / 32 + 1) : 0;
-  u32x4 kop[8], vop[8];
-  f32x4 sc[NT][2];
-  u32x4 pb[NT];
-  bool first_pass = true;
-
-  auto phase_m = [&](int c) {
-    const bool do_qk = c >= 0 && c < ncomp;
-    const bool do_pv = c >= 1 && c - 1 < ncomp;
-    if (!do_qk && !do_pv) return;
-    __builtin_amdgcn_s_setprio(1);
-    // the V^T operands of chunk c-1 land while the S^T tiles are computed
-    if (do_pv) {
-      lds_read_v(lds_lane_addr(slot(c - 1), lane), vop);
-      wait_lds_but8_for(kop);
-    } else {
-      wait_lds_for(kop);
-    }
-    if (do_qk) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          sc[nt][0] = mfma(kop[k], qb[nt][k], sc[nt][0]);
-          sc[nt][1] = mfma(kop[4 + k], qb[nt][k], sc[nt][1]);
-        }
-    }
-    if (do_pv) {
-      wait_lds_for(vop);
-      const int key0 = it.k0 + 32 * (c - 1);
-      if (key0 + 32 > it.k1) {
-        // keys past the tile may hold stale data: zero their values
-        const int nv = it.k1 - (key0 + 8 * g);
-        u32x4 keep;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(vop[dt], pb[nt], acc[nt][dt]);
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  auto phase_v = [&](int c) {
-    // reads for the next matrix phase first, so they land during the softmax
-    if (c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(c + 1), lane), kop);
-    if (c < 0 || c >= ncomp) return;
-    const int key0 = it.k0 + 32 * c;
-    const int kl = key0 + 8 * g;
-    float sv[NT][8];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[nt][i] = sc[nt][0][i];
-        sv[nt][4 + i] = sc[nt][1][i];
-      }
-    // causal masking is needed only where a key can lie past a column's
-    // position (or past the tile, or on empty columns)
-    if (key0 + 31 > wpos0 || wnp < WP || key0 + 32 > it.k1) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = kl + j;
-          sv[nt][j] = (col_ok[nt] && key < it.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
-        }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      m_hi[nt] = max3(max3(max3(m_hi[nt], sv[nt][0], sv[nt][1]), max3(sv[nt][2], sv[nt][3], sv[nt][4]),
-                           sv[nt][5]),
-                      sv[nt][6], sv[nt][7]);
-    if (c == 0 && first_pass) {
-      // the reference: the column's maximum over the first chunk
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float mx = xmax32(xmax16(m_hi[nt]));
-        neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[nt][i] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i], c2, neg_ref[nt])),
-                              __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * i + 1], c2, neg_ref[nt])));
-        l_part[nt] = sum_bf16x2(pb[nt][i], l_part[nt]);
-      }
-  };
-
   auto barrier = [] {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // Two groups of four wavefronts (one of each per SIMD) run half a step
+  // apart for the whole list.  A wavefront alternates a vector phase V(c) --
+  // the probabilities of chunk c, while the K operands of chunk c+1 land --
+  // with a matrix phase M(c+1) -- S^T tiles of chunk c+1 and O^T += V^T P^T
+  // of chunk c.  Group 1 passes one extra barrier first (group 0 one extra
+  // at the end), so it runs V(c) while group 0 runs M(c+1) and M(c+1) while
+  // group 0 runs V(c+1): each SIMD's matrix core works for one wavefront
+  // while the other computes exponentials.  A tile of n chunks takes n + 1
+  // steps of two barriers; chunk c (stream index) occupies its slot from the
+  // barrier before group 0's V(c-1) to group 1's M(c+1), and the load issued
+  // at a step goes kAhead chunks ahead, into the slot of a chunk three steps
+  // older -- also across tile boundaries, where the stream simply goes on.
+  const int grp = w >> 2;
+  for (int c = 0; c < kAhead; ++c) issue_next();
+  if (grp == 1) barrier();
+
+  int g_base = 0;        // stream index of the current tile's first chunk
+  uint64_t redo = 0;     // list positions < 64 whose columns need recomputing
+  bool redo_all = false; // a later position does (recompute every tile)
+  WideTile dn = wide_tile(a, i0);  // the next tile's descriptor, fetched a tile ahead
+  for (int i = i0; i < i1; ++i) {
+    const WideTile d = dn;
+    if (i + 1 < i1) dn = wide_tile(a, i + 1);
+    const int wpos0 = d.pos0 + w * WP;  // first position of this wavefront
+    const int wnp = max(0, min(WP, d.np - w * WP));
+    const int wlast = wpos0 + wnp - 1;
+    const int ncomp = wnp > 0 ? min(d.nch, (wlast >> 5) + 1) : 0;
+
+    bool col_ok[NT];
+    int col_pos[NT];
+    int64_t col_qoff[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + r;
+      const int pc = col >> a.log2G;
+      const int ho = col & (G - 1);
+      col_ok[nt] = pc < wnp;
+      col_pos[nt] = wpos0 + pc;
+      col_qoff[nt] = ((int64_t)(d.t0 + w * WP + pc) * a.Hq + d.kvh * G + ho) * D;
+    }
+    // Q^T operands; columns past the tile read the zero tile (no branch, so
+    // the loads' registers are never written by anything else)
+    u32x4 qb[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint16_t *qp = (col_ok[nt] ? a.q + col_qoff[nt] : a.zero) + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qb[nt][c] = load16(qp + 32 * c);
+    }
+
+    // Probabilities are taken relative to a fixed per-column reference: the
+    // column's maximum score in the tile's first chunk (key 0 is in it).
+    // fp32 and bf16 keep 8 exponent bits, so later scores may exceed it by
+    // up to kRedoLog2 without overflow and nothing is rescaled -- the
+    // accumulators never leave the matrix cores inside the loop.  Each lane
+    // tracks the largest raw score it sees; a wavefront with a column past
+    // the margin recomputes its columns after the list (exactly, with the
+    // running-maximum softmax of the narrow path).
+    f32x4 acc[NT][8];
+    float neg_ref[NT];  // -(reference) in log2 units
+    float m_hi[NT];     // this lane's largest raw score
+    float l_part[NT];   // this lane's sum of its rounded probabilities
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       l_part[nt] = 0.f;
+      m_hi[nt] = neg_inf();
+      neg_ref[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (pass == 0) {
-        m_hi[nt] = neg_inf();
-        neg_ref[nt] = 0.f;
+    }
+    u32x4 kop[8], vop[8];
+    f32x4 sc[NT][2];
+    u32x4 pb[NT];
+
+    auto phase_m = [&](int c) {
+      const bool do_qk = c >= 0 && c < ncomp;
+      const bool do_pv = c >= 1 && c - 1 < ncomp;
+      if (!do_qk && !do_pv) return;
+      __builtin_amdgcn_s_setprio(1);
+      // the V^T operands of chunk c-1 land while the S^T tiles are computed
+      if (do_pv) {
+        lds_read_v(lds_lane_addr(slot(g_base + c - 1), lane), vop);
+        wait_lds_but8_for(kop);
+      } else {
+        wait_lds_for(kop);
       }
-    }
-    if (pass == 0) {
-      if (w == 0 && lane == 0) lds_restart = 0;
-      __syncthreads();
-    }
-    // Chunk c lives in slot c % kNbuf from the barrier before group 0's
-    // V(c-1) (which reads its K) to group 1's M(c+1) (which reads its V^T);
-    // three steps after its first use the slot takes chunk c + kNbuf.
-    // Group 0 loads the K regions and group 1, half a step later, the V^T
-    // regions, which are first read a step after the K regions of the chunk.
-    for (int c = 0; c < kAhead && c < nchunks; ++c) issue(c);
-    if (grp == 1) barrier();
-    for (int s = 0; s <= nchunks; ++s) {
-      // every LDS read of this wavefront is done (its slot may be refilled)
-      // and its loads of chunk s have landed; chunks s+1 .. s+kAhead-1 may fly
+      if (do_qk) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            sc[nt][0] = mfma(kop[k], qb[nt][k], sc[nt][0]);
+            sc[nt][1] = mfma(kop[4 + k], qb[nt][k], sc[nt][1]);
+          }
+      }
+      if (do_pv) {
+        wait_lds_for(vop);
+        const int key0 = 32 * (c - 1);
+        if (key0 + 32 > d.k1) {
+          // keys past the tile may hold stale data: zero their values
+          const int nv = d.k1 - (key0 + 8 * g);
+          u32x4 keep;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            keep[e] = (2 * e < nv ? 0x0000FFFFu : 0u) | (2 * e + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) vop[dt] &= keep;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][dt] = mfma(vop[dt], pb[nt], acc[nt][dt]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto phase_v = [&](int c) {
+      // reads for the next matrix phase first, so they land during the softmax
+      if (c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(g_base + c + 1), lane), kop);
+      if (c < 0 || c >= ncomp) return;
+      const int key0 = 32 * c;
+      const int kl = key0 + 8 * g;
+      float sv[NT][8];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[nt][e] = sc[nt][0][e];
+          sv[nt][4 + e] = sc[nt][1][e];
+        }
+      // causal masking is needed only where a key can lie past a column's
+      // position (or past the tile, or on empty columns)
+      if (key0 + 31 > wpos0 || wnp < WP || key0 + 32 > d.k1) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int key = kl + j;
+            sv[nt][j] = (col_ok[nt] && key < d.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
+          }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        m_hi[nt] = max3(max3(max3(m_hi[nt], sv[nt][0], sv[nt][1]), max3(sv[nt][2], sv[nt][3], sv[nt][4]),
+                             sv[nt][5]),
+                        sv[nt][6], sv[nt][7]);
+      if (c == 0) {
+        // the reference: the column's maximum over the first chunk
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float mx = xmax32(xmax16(m_hi[nt]));
+          neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[nt][e] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * e], c2, neg_ref[nt])),
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * e + 1], c2, neg_ref[nt])));
+          l_part[nt] = sum_bf16x2(pb[nt][e], l_part[nt]);
+        }
+    };
+
+    // Each step: every LDS read of this wavefront is done (its slot may be
+    // refilled) and its loads of the tile's chunk s have landed -- the
+    // stream's next kAhead - 1 chunks, issued after it, may still fly.  The
+    // issue of chunk s is followed by exactly kLoadsPerIssue loads per later
+    // chunk (and, at step 0, by the Q loads, which the wait then also
+    // covers).
+    auto wait_chunk = [&](int s) {
       wait_lds();
-      switch (min(nchunks - 1 - s, kAhead - 1)) {
-        case 4: wait_vmcnt<4 * RPW>(); break;
-        case 3: wait_vmcnt<3 * RPW>(); break;
-        case 2: wait_vmcnt<2 * RPW>(); break;
-        case 1: wait_vmcnt<RPW>(); break;
+      switch (n_issued - 1 - (g_base + s)) {
+        case 4: wait_vmcnt<4 * kLoadsPerIssue>(); break;
+        case 3: wait_vmcnt<3 * kLoadsPerIssue>(); break;
+        case 2: wait_vmcnt<2 * kLoadsPerIssue>(); break;
+        case 1: wait_vmcnt<kLoadsPerIssue>(); break;
         default: wait_vmcnt<0>(); break;
       }
+    };
+    // step 0 (a tile has at least one chunk)
+    wait_chunk(0);
+    barrier();
+    issue_next();
+    phase_v(-1);
+    barrier();
+    q_ready(qb);
+    phase_m(0);
+    for (int s = 1; s <= d.nch; ++s) {
+      if (s < d.nch) wait_chunk(s);
+      else wait_lds();
       barrier();
-      if (s + kAhead < nchunks) issue(s + kAhead);
+      if (s < d.nch) issue_next();
       phase_v(s - 1);
       barrier();
       phase_m(s);
     }
-    if (grp == 0) barrier();
-    if (pass == 1) break;
-    // did any column of any wavefront outgrow its reference by 2^100?
-    bool grew = false;
+
+    // did a column outgrow its reference?  (rare: recomputed after the list)
+    {
+      bool grew = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) grew |= __builtin_fmaf(m_hi[nt], c2, neg_ref[nt]) > 100.f;
-    if (__builtin_amdgcn_ballot_w64(grew) && lane == 0) atomicOr(&lds_restart, 1);
-    __syncthreads();
-    const bool again = lds_restart != 0;
-    __syncthreads();
-    if (!again) break;
-    // second pass: the exact maximum of the first is the reference
+      for (int nt = 0; nt < NT; ++nt) grew |= __builtin_fmaf(m_hi[nt], c2, neg_ref[nt]) > kRedoLog2;
+      if (__builtin_amdgcn_ballot_w64(grew)) {
+        if (i - i0 < 64) redo |= 1ull << (i - i0);
+        else redo_all = true;
+      }
+    }
+
+    // epilogue: column sums over the four lane groups, then O / l
+    float l_tot[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float mx = xmax32(xmax16(m_hi[nt]));
-      neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
+      if (!col_ok[nt]) continue;
+      const float inv = 1.f / l_tot[nt];
+      uint16_t *op = a.out + col_qoff[nt] + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 v = acc[nt][dt] * inv;
+        u32x2 o;
+        o[0] = pack_bf16(v[0], v[1]);
+        o[1] = pack_bf16(v[2], v[3]);
+        *reinterpret_cast<u32x2 *>(op + 16 * dt) = o;
+      }
     }
-    first_pass = false;
+    g_base += d.nch;
   }
+  if (grp == 0) barrier();
+  // the stream's trailing zero chunks land before the workgroup's LDS is
+  // released
+  wait_vmcnt<0>();
 
-  // epilogue: column sums over the four lane groups, then O / l
-  float l_tot[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (!col_ok[nt]) continue;
-    const float inv = 1.f / l_tot[nt];
-    uint16_t *op = a.out + col_qoff[nt] + 4 * g;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 v = acc[nt][dt] * inv;
-      u32x2 o;
-      o[0] = pack_bf16(v[0], v[1]);
-      o[1] = pack_bf16(v[2], v[3]);
-      *reinterpret_cast<u32x2 *>(op + 16 * dt) = o;
+  // Recompute the columns of any tile that outgrew its references, as
+  // narrow items (up to 16 columns each, keys from HBM, running maximum);
+  // they overwrite the tile's output.  No barriers: wavefronts are
+  // independent from here on.
+  if (redo == 0 && !redo_all) return;
+  for (int i = i0; i < i1; ++i) {
+    if (!redo_all && !(i - i0 < 64 && ((redo >> (i - i0)) & 1))) continue;
+    const WideTile d = wide_tile(a, i);
+    const int wnp = max(0, min(WP, d.np - w * WP));
+    const int per = pkv::kTileCols >> a.log2G;  // positions per narrow item
+    for (int p = 0; p < wnp; p += per) {
+      Item it;
+      it.seq = d.seq;
+      it.kvh = d.kvh;
+      it.t0 = d.t0 + w * WP + p;
+      it.np = min(per, wnp - p);
+      it.pos0 = d.pos0 + w * WP + p;
+      it.k0 = 0;
+      it.k1 = it.pos0 + it.np;
+      it.part = -1;
+      run_item<1>(a, it);
     }
   }
 }
@@ -819,48 +918,36 @@ void attention_kernel(AttnArgs a) {
   }
 }
 
-// Mixed launch.  Workgroups come in rows of eight (consecutive workgroups
-// go to the eight XCDs in turn).  narrow_rows rows, spread evenly over the
-// first 32 rows (the workgroups that start at once, one per CU), carry eight
-// narrow wavefronts each, walking their item shares; every other row holds
-// eight wide tiles in item order (longest first), so wide item i runs on
-// XCD i % 8 and the tiles of a kv head share an L2.  The bandwidth-bound
-// narrow shares thus stream on some CUs while the others work through the
-// matrix-bound wide tiles, and a CU whose narrow workgroup ends takes the
-// next wide tile.
-__device__ __forceinline__ void mixed_row(int rows, int narrow_rows, int rho, bool &narrow, int &ord) {
-  const int S = min(32, rows);  // rows started at once
-  if (rho < S) {
-    const int lo = rho * narrow_rows / S, hi = (rho + 1) * narrow_rows / S;
-    narrow = hi > lo;
-    ord = narrow ? lo : rho - lo;
-  } else {
-    narrow = false;
-    ord = rho - narrow_rows;
-  }
-}
-
+// Launch with wide tiles: a fixed grid of persistent workgroups in rows of
+// eight (consecutive workgroups go to the eight XCDs in turn).  The narrow
+// rows (spread evenly over the grid) first walk their wavefronts' narrow
+// shares -- bandwidth-bound streams beside the other CUs' matrix-bound wide
+// tiles -- and then, like every other workgroup, the wide tiles of their
+// list; the lists are balanced and keep each kv head's tiles on one XCD.
 __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(AttnArgs a) {
   static_assert(pkv::kWideWaves == 8, "rows of eight workgroups of eight wavefronts");
-  const int rows = a.narrow_rows + (a.num_wide + 7) / 8;
-  bool narrow;
-  int ord;
-  mixed_row(rows, a.narrow_rows, blockIdx.x / 8, narrow, ord);
-  const int wg = ord * 8 + blockIdx.x % 8;
-  if (!narrow) {
-    if (wg >= a.num_wide) return;
-    const Item it = load_item(a, wg);
-    if (it.k1 > it.k0 && it.np > 0) run_wide_tile(a, it);
-    return;
+  const int j = blockIdx.x;
+  if (j >= a.num_wg) return;
+  const pkv::RowRole role = pkv::mixed_row(a.num_wg / 8, a.narrow_rows, j / 8);
+  if (role.narrow) {
+    // narrow wavefronts use no LDS and no barriers, so the wide loop below
+    // may start on some wavefronts while others still stream
+    const int w = (role.ord * 8 + j % 8) * 8 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < a.num_waves) {
+      const int i0 = a.num_wide + sload(a.waves, w);
+      const int i1 = a.num_wide + sload(a.waves, w + 1);
+      for (int i = i0; i < i1; ++i) {
+        const Item it = load_item(a, i);
+        if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
+      }
+    }
+    // nothing of the narrow walk stays in flight: the wide loop's own waits
+    // are then the only ones its tile loop needs
+    wait_vmcnt<0>();
   }
-  const int w = wg * 8 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w >= a.num_waves) return;
-  const int i0 = a.num_wide + sload(a.waves, w);
-  const int i1 = a.num_wide + sload(a.waves, w + 1);
-  for (int i = i0; i < i1; ++i) {
-    const Item it = load_item(a, i);
-    if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
-  }
+  const int i0 = sload(a.wg_list, j);
+  const int i1 = sload(a.wg_list, j + 1);
+  if (i0 < i1) run_wide_list(a, i0, i1);
 }
 
 // ---------------------------------------------------------------------------
@@ -928,7 +1015,7 @@ const char *pkv_status_string(int status) {
   }
 }
 
-int pkv_version(void) { return 101; }
+int pkv_version(void) { return 102; }
 
 int pkv_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                      const int32_t *block_tables, int32_t bt_stride, int32_t num_seqs,
@@ -985,6 +1072,8 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.part_ml = reinterpret_cast<float2 *>(w + plan->ml_off);
   a.part_o = reinterpret_cast<float *>(w + plan->o_off);
   a.zero = reinterpret_cast<const uint16_t *>(w + plan->zero_off);
+  a.wg_list = nullptr;
+  a.num_wg = 0;
   a.narrow_rows = plan->narrow_rows;
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
@@ -997,10 +1086,14 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.scale_log2 = scale * 1.4426950408889634f;
   if (a.log2G < 0) return PKV_EUNSUPPORTED;
   if (plan->num_wide_items > 0) {
-    if (plan->narrow_rows < 0 || plan->narrow_rows > 32 || (int64_t)plan->narrow_rows * 64 < plan->num_waves)
+    const int nwg = plan->num_workgroups;
+    if (nwg <= 0 || nwg % 8 != 0 || nwg > 256 || plan->narrow_rows < 0 || plan->narrow_rows > nwg / 8 ||
+        (int64_t)plan->narrow_rows * 64 < plan->num_waves || plan->wg_off < 0 ||
+        (size_t)plan->wg_off + (size_t)(nwg + 1) * 4 > plan->ws_bytes)
       return PKV_EINVAL;
-    const int64_t rows = plan->narrow_rows + ((int64_t)plan->num_wide_items + 7) / 8;
-    hipLaunchKernelGGL(attention_mixed_kernel, dim3((unsigned)(rows * 8)), dim3(64 * pkv::kWideWaves), 0,
+    a.wg_list = reinterpret_cast<const int32_t *>(w + plan->wg_off);
+    a.num_wg = nwg;
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
                        as_stream(stream), a);
   } else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);

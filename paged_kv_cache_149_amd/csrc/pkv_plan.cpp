@@ -5,8 +5,13 @@
 //  * q_len > 1 (prefill / chunked prefill, causal offset = cached prefix:
 //    "Continuous Batching 深入实现", section "一个 chunked prefill 请求怎么组织
 //    attention"): tiles of query positions x the kv head's query heads.  A
-//    wide tile (up to 4 x 64/G positions: four wavefronts of 64 columns
-//    sharing K/V through LDS) is one workgroup's whole item, placed first.
+//    wide tile (256 columns: 256/G positions x G heads) is computed by a
+//    whole workgroup of eight wavefronts sharing K/V through LDS.  The
+//    launch has a fixed set of persistent workgroups; the wide tiles are
+//    dealt to them longest first, each to the least loaded workgroup (with
+//    the estimated time of its narrow share as its starting load), tiles of
+//    kv head h to the workgroups on XCD h % 8, so a head's keys and values
+//    are fetched from HBM into one L2.
 //  * Decode rows and the short tails of prefill rows: narrow (<= 16 column)
 //    units (tile, kv head), each a stream of 32-key chunks.  All chunks of all
 //    units are dealt out in equal contiguous shares to a fixed number of
@@ -30,8 +35,16 @@ using pkv::Merge;
 
 constexpr int kDefaultNarrowWaves = 1024;  // one per SIMD on 256 CUs
 constexpr int kDefaultMinWaveKeys = 512;
+constexpr int kDefaultWorkgroups = 256;    // one per CU on an MI355X
+constexpr int kXcds = 8;                   // consecutive workgroups go to the XCDs in turn
 
-int round_up32(int64_t x) { return (int)((x + 31) / 32 * 32); }
+// Cost model of the launch with wide tiles, in CU-microseconds (measured on
+// MI355X): a wide tile costs ~1.1 us per 32-key chunk plus ~2 us to start;
+// a narrow workgroup streams its 32-key chunks (16 KiB of K and V) at
+// ~30 GB/s per CU.
+constexpr double kWideChunkUs = 1.1;
+constexpr double kWideTileUs = 2.0;
+constexpr double kNarrowChunkUs = 16384.0 / 30.0e3;
 
 }  // namespace
 
@@ -106,9 +119,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   std::vector<int32_t> wave_off;
   int64_t part_cols = 0;
 
-  // wide tiles: one item each, longest first
-  std::stable_sort(wide_tiles.begin(), wide_tiles.end(),
-                   [](const Tile &x, const Tile &y) { return x.keys > y.keys; });
+  // wide tiles: one item per (tile, kv head); dealt to workgroups below
   for (const Tile &t : wide_tiles)
     for (int h = 0; h < Hkv; ++h) items.push_back(Item{t.seq, h, t.t0, t.np, t.pos0, 0, t.keys, -1});
   const int n_wide = (int)items.size();
@@ -118,23 +129,24 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   int64_t total_chunks = 0;
   for (const Tile &t : narrow_tiles) total_chunks += (int64_t)Hkv * ((t.keys + 31) / 32);
 
-  // Narrow wavefronts.  Alone they are one per SIMD.  In a mixed launch they
-  // travel in rows of eight workgroups of eight, started beside the wide
-  // tiles; the rows get the share of the chip the narrow work is estimated
-  // to need: wide tiles at ~1 PFLOP/s, narrow 32-key chunks (K and V of one
-  // kv head, 16 KiB) at ~6 TB/s.
+  // Narrow wavefronts.  Alone they are one per SIMD.  Beside wide tiles
+  // they travel in rows of eight workgroups of eight wavefronts, whose CUs
+  // afterwards join the wide tiles; the rows get the share of the chip the
+  // narrow work is estimated to need.
+  const int max_wg = (opts && opts->workgroups > 0) ? opts->workgroups : kDefaultWorkgroups;
+  if (max_wg % kXcds != 0 || max_wg > kDefaultWorkgroups) return PKV_EINVAL;
+  const int max_rows = max_wg / kXcds;
+  double wide_us = 0;
+  for (int i = 0; i < n_wide; ++i) wide_us += kWideChunkUs * ((items[i].k1 + 31) / 32) + kWideTileUs;
   int narrow_rows = 0;
   int want_waves = kDefaultNarrowWaves;
   if (n_wide > 0 && total_chunks > 0) {
-    double wide_flop = 0;
-    for (int i = 0; i < n_wide; ++i)
-      wide_flop += 4.0 * head_dim * G * (double)items[i].np * (items[i].k1 - items[i].k0);
-    const double tw = wide_flop / 1.0e15, tn = (double)total_chunks * 32 * 4 * head_dim / 6.0e12;
-    narrow_rows = std::max(1, std::min(32, (int)(32.0 * tn / (tw + tn) + 0.5)));
+    const double narrow_us = (double)total_chunks * kNarrowChunkUs;
+    narrow_rows = std::max(1, std::min(max_rows, (int)(max_rows * narrow_us / (narrow_us + wide_us) + 0.5)));
     want_waves = 64 * narrow_rows;
   }
   if (opts && opts->narrow_waves > 0) want_waves = opts->narrow_waves;
-  if (n_wide > 0) want_waves = std::min(want_waves, 64 * 32);
+  if (n_wide > 0) want_waves = std::min(want_waves, 64 * max_rows);
   int W = 0;
   int wave_keys = 0;
   if (total_chunks > 0) {
@@ -142,6 +154,41 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     W = (int)std::max<int64_t>(1, std::min<int64_t>(want_waves, by_size));
     wave_keys = (int)((total_chunks + W - 1) / W * 32);
     if (n_wide > 0) narrow_rows = (W + 63) / 64;
+  }
+
+  // Persistent workgroups and their wide-tile lists.
+  int n_wg = 0;
+  std::vector<int32_t> wg_list;
+  if (n_wide > 0) {
+    const int rows = std::min(max_rows, narrow_rows + (n_wide + kXcds - 1) / kXcds);
+    n_wg = rows * kXcds;
+    // starting load: the narrow share of a narrow workgroup (eight wavefronts)
+    const double share_us = W > 0 ? 8.0 * ((total_chunks + W - 1) / W) * kNarrowChunkUs : 0.0;
+    std::vector<double> load(n_wg, 0.0);
+    for (int j = 0; j < n_wg; ++j) {
+      if (pkv::mixed_row(rows, narrow_rows, j / kXcds).narrow) load[j] = share_us;
+    }
+    // tiles of kv head h go to XCD h % 8 when every XCD gets whole heads
+    const bool affine = Hkv % kXcds == 0;
+    std::vector<int> order(n_wide);
+    for (int i = 0; i < n_wide; ++i) order[i] = i;
+    auto cost = [&](int i) { return kWideChunkUs * ((items[i].k1 + 31) / 32) + kWideTileUs; };
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost(x) > cost(y); });
+    std::vector<std::vector<int>> lists(n_wg);
+    for (int i : order) {
+      int best = -1;
+      for (int j = affine ? items[i].kvh % kXcds : 0; j < n_wg; j += affine ? kXcds : 1)
+        if (best < 0 || load[j] < load[best]) best = j;
+      load[best] += cost(i);
+      lists[best].push_back(i);
+    }
+    std::vector<Item> wide(items.begin(), items.begin() + n_wide);
+    wg_list.push_back(0);
+    int k = 0;
+    for (int j = 0; j < n_wg; ++j) {
+      for (int i : lists[j]) items[k++] = wide[i];
+      wg_list.push_back(k);
+    }
   }
   auto unit_tile = [&](int64_t u) -> const Tile & { return narrow_tiles[u / Hkv]; };
   auto unit_chunks = [&](int64_t u) -> int { return (unit_tile(u).keys + 31) / 32; };
@@ -213,20 +260,23 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   plan->wave_keys = wave_keys;
   plan->kv_keys = kv_keys;
   plan->visible_pairs = pairs;
+  plan->num_workgroups = n_wg;
   const size_t items_b = pkv::align_up(items.size() * sizeof(Item));
   const size_t waves_b = pkv::align_up(wave_off.size() * sizeof(int32_t));
   const size_t merge_b = pkv::align_up(merges.size() * sizeof(Merge));
+  const size_t wg_b = pkv::align_up(wg_list.size() * sizeof(int32_t));
   // a zero (block, head) tile: loads of table entries outside [0, num_blocks)
   // are pointed at it
   const size_t zero_b = (size_t)pkv::kBlock * pkv::kHeadDim * 2;
   plan->items_off = 0;
   plan->waves_off = (int64_t)items_b;
   plan->merge_off = (int64_t)(items_b + waves_b);
-  plan->zero_off = (int64_t)(items_b + waves_b + merge_b);
+  plan->wg_off = (int64_t)(items_b + waves_b + merge_b);
+  plan->zero_off = plan->wg_off + (int64_t)wg_b;
   plan->ml_off = plan->zero_off + (int64_t)zero_b;
   plan->o_off = plan->ml_off + (int64_t)pkv::align_up((size_t)part_cols * 8);
   plan->ws_bytes = (size_t)plan->o_off + (size_t)part_cols * pkv::kHeadDim * 4;
-  plan->host_bytes = items_b + waves_b + merge_b + zero_b;
+  plan->host_bytes = items_b + waves_b + merge_b + wg_b + zero_b;
   if (!h_staging) return PKV_OK;  // size query
   if (h_staging_bytes < plan->host_bytes) return PKV_EWORKSPACE;
   if (ws && ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
@@ -235,6 +285,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   if (!items.empty()) std::memcpy(hs, items.data(), items.size() * sizeof(Item));
   if (!wave_off.empty()) std::memcpy(hs + items_b, wave_off.data(), wave_off.size() * sizeof(int32_t));
   if (!merges.empty()) std::memcpy(hs + items_b + waves_b, merges.data(), merges.size() * sizeof(Merge));
+  if (!wg_list.empty()) std::memcpy(hs + plan->wg_off, wg_list.data(), wg_list.size() * sizeof(int32_t));
   std::memset(hs + plan->zero_off, 0, zero_b);
   if (ws && plan->host_bytes > 0) {
     hipError_t e = hipMemcpyAsync(ws, h_staging, plan->host_bytes, hipMemcpyHostToDevice,

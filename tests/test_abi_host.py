@@ -89,9 +89,61 @@ def test_plan_wide_items_first_then_balanced_waves():
     wide = it[:, 3] * 4 > 16
     nw = plan.num_wide_items
     assert nw > 0 and wide[:nw].all() and not wide[nw:].any()
-    lens = it[:nw, 6] - it[:nw, 5]
-    assert (np.diff(lens) <= 0).all()
+    _check_wg_lists(plan)
     _check_waves(plan)
+
+
+def _check_wg_lists(plan, affine=True, slack=None):
+    """The persistent workgroups' lists tile the wide items exactly once;
+    with Hkv a multiple of 8 every tile of kv head h sits on a workgroup of
+    XCD h % 8 (workgroup j runs on XCD j % 8); the estimated loads (the
+    planner's cost model, narrow shares included) are balanced to within
+    the largest single tile."""
+    nwg = plan.num_workgroups
+    off = plan.wg_lists()
+    it = plan.items()
+    nw = plan.num_wide_items
+    assert nwg % 8 == 0 and 0 < nwg <= 256 and len(off) == nwg + 1
+    assert off[0] == 0 and off[-1] == nw and (np.diff(off) >= 0).all()
+    assert (it[:nw, 5] == 0).all() and (it[:nw, 7] == -1).all()
+    cost = 1.1 * ((it[:nw, 6] + 31) // 32) + 2.0
+    rows = nwg // 8
+    nr = plan.narrow_rows
+    share = 8.0 * (plan.wave_keys // 32) * 16384.0 / 30e3 if plan.num_waves else 0.0
+    loads = []
+    for j in range(nwg):
+        rho = j // 8
+        narrow = (rho + 1) * nr // rows > rho * nr // rows
+        lo, hi = off[j], off[j + 1]
+        if affine:
+            assert (it[lo:hi, 1] % 8 == j % 8).all()
+        loads.append((share if narrow else 0.0) + cost[lo:hi].sum())
+    if slack is None:
+        slack = cost.max() + share
+    for x in range(8 if affine else 1):
+        grp = [loads[j] for j in range(nwg) if not affine or j % 8 == x]
+        assert max(grp) - min(grp) <= slack + 1e-9, (x, max(grp), min(grp))
+
+
+@pytest.mark.parametrize("name,seqs", [
+    ("fresh", [(0, 2048)] * 4),
+    ("chunk-after-prefix", [(30720, 2048)]),
+    ("trace-like", [(0, 700), (300, 250), (0, 1500), (5000, 1), (200, 1), (0, 33), (1000, 90)]),
+])
+def test_plan_wide_tiles_dealt_to_persistent_workgroups(name, seqs):
+    b = wl.make_batch(name, seqs, seed=3, pool="lazy")
+    plan = _plan(b.cu_seqlens_q, b.seq_lens)
+    assert plan.num_wide_items > 0
+    _check_wg_lists(plan)
+    _coverage(plan, b.cu_seqlens_q, b.seq_lens, 32, 8)
+    for wg in (8, 64):
+        p = _plan(b.cu_seqlens_q, b.seq_lens, workgroups=wg)
+        assert p.num_workgroups <= wg
+        _check_wg_lists(p)
+    p = _plan(b.cu_seqlens_q, b.seq_lens, Hq=8, Hkv=2)
+    _check_wg_lists(p, affine=False)
+    with pytest.raises(binding.PKVError):
+        _plan(b.cu_seqlens_q, b.seq_lens, workgroups=12)
 
 
 def _check_waves(plan):

@@ -222,6 +222,8 @@ def test_gqa_ratios(dev, Hq, Hkv):
     {"min_wave_keys": 32, "narrow_waves": 1 << 20},   # one 32-key chunk per wavefront
     {"min_wave_keys": 64, "narrow_waves": 3, "wide_tiles": 0},  # three wavefronts walk everything
     {"wide_tiles": 1},
+    {"workgroups": 8},                                 # long wide lists: many tile boundaries
+    {"workgroups": 16, "narrow_waves": 64, "wide_tiles": 1},
 ])
 def test_plan_options_same_result(dev, opts):
     b = wl.make_batch("opts", [(700, 1), (0, 50), (90, 3), (2000, 1), (129, 20)], seed=33)
@@ -242,6 +244,32 @@ def test_nan_in_unused_slots_does_not_leak(dev):
             b.v_pool[last, :, o::16] = 0x7FC0
     out, _, _, _ = run_step(b, dev)
     check_attention(out, oracle.packed_attention(b), "nan tails")
+
+
+def test_growing_scores_recompute(dev):
+    """Scores that grow by ~2 (log2 units) every 32 keys: a prefill tile's
+    first-chunk reference is exceeded by more than 2^100 after ~50 chunks,
+    so the wavefronts of such tiles recompute their columns with the
+    running-maximum softmax.  Every query is 1.0; key p is 0.125 * (p // 32)
+    in every dimension."""
+    seqs = [(0, 3000), (2900, 100), (3100, 1)]
+    b = wl.make_batch("growing-scores", seqs, seed=35, pool="materialize")
+    D = b.head_dim
+    one = wl.f32_to_bf16_bits(np.float32(1.0))
+    b.q[:] = one
+    kval = lambda p: wl.f32_to_bf16_bits(np.float32(0.125 * (p // 32)))
+    cu = b.cu_seqlens_q
+    for s, (c, ql) in enumerate(seqs):
+        for p in range(c):
+            blk = int(b.block_tables[s, p // 16])
+            b.k_pool[blk, :, (p % 16) * D:(p % 16 + 1) * D] = kval(p)
+        for j in range(ql):
+            b.k_new[cu[s] + j] = kval(c + j)
+    note("growing scores")
+    out, slots, t, plan = run_step(b, dev)
+    assert plan.num_wide_items > 0
+    check_append(b, slots, t)
+    check_attention(out, oracle.packed_attention(b), "growing scores")
 
 
 def test_attention_entry_points_agree(dev):
