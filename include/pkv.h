@@ -34,10 +34,13 @@
  *
  * Paged pool layout (the pages fix only the slot translation and that a
  * block's 16 tokens are contiguous; they leave the tensor layout open):
- *   k_cache : bf16[num_blocks][Hkv][16][128]   token-major 4 KiB tiles
- *   v_cache : bf16[num_blocks][Hkv][128][16]   dimension-major 4 KiB tiles
+ *   k_cache : bf16[num_blocks][Hkv][4][16][32]  4 KiB tiles: four groups of
+ *             32 dimensions, each group token-major
+ *   v_cache : bf16[num_blocks][Hkv][128][16]    dimension-major 4 KiB tiles
  * Slot x is block x / 16, offset x % 16.  Key element (o, d) of a tile sits
- * at o * 128 + d; value element (o, d) at d * 16 + o.
+ * at (d / 32) * 512 + o * 32 + d % 32; value element (o, d) at d * 16 + o.
+ * (Both orders let a 16-byte-per-lane load over 16 tokens read whole cache
+ * lines in the operand order of the bf16 MFMAs.)
  *
  * Packed tensors:
  *   q        : bf16[T][Hq][128]      k_new, v_new : bf16[T][Hkv][128]

@@ -15,6 +15,7 @@ from .paged_attention import (  # noqa: F401
     bf16_bits_to_f64,
     slot_of,
     slot_mapping,
+    k_group,
     read_k_token,
     read_v_token,
     gather_kv,

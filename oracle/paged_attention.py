@@ -30,10 +30,11 @@ the design notes):
   ``c_s .. seq_lens[s] - 1``.
 * Physical layout of a (block, kv head) tile of the pool (the pages fix the
   slot formula and that a block's 16 tokens are contiguous, and defer the
-  tensor layout to a section that is not present): K tiles are token-major,
-  element (o, d) at ``o * D + d``; V tiles are dimension-major, element
-  (o, d) at ``d * 16 + o``.  Slot ``x`` is block ``x // 16``, offset
-  ``x % 16``.
+  tensor layout to a section that is not present): K tiles hold the
+  dimensions in groups of W = min(32, D), each group token-major: element
+  (o, d) at ``(d // W) * 16 * W + o * W + d % W`` (D = 128: four groups of
+  32 dimensions); V tiles are dimension-major, element (o, d) at
+  ``d * 16 + o``.  Slot ``x`` is block ``x // 16``, offset ``x % 16``.
 * Masked scores are -inf (the M_ij formula of [K4I]); every row sees at
   least its own key, so no row is fully masked.
 
@@ -91,11 +92,18 @@ def slot_mapping(cu_seqlens_q, seq_lens, block_tables) -> np.ndarray:
 # reading the pool (layout reading stated in the module docstring)
 # ----------------------------------------------------------------------------
 
+def k_group(D: int) -> int:
+    """Width of the dimension groups of a K tile."""
+    return min(32, D)
+
+
 def read_k_token(k_pool: np.ndarray, slot: int, head: int, D: int) -> np.ndarray:
-    """The D key elements at ``slot`` for kv head ``head`` (bf16 bits)."""
+    """The D key elements at ``slot`` for kv head ``head`` (bf16 bits): in
+    each group of W dimensions, token o's W elements start at o * W."""
     b, o = divmod(int(slot), BLOCK)
-    tile = k_pool[b, head]
-    return tile[o * D:(o + 1) * D]
+    W = k_group(D)
+    tile = np.asarray(k_pool[b, head]).reshape(D // W, BLOCK, W)
+    return tile[:, o, :].reshape(D)
 
 
 def read_v_token(v_pool: np.ndarray, slot: int, head: int, D: int) -> np.ndarray:
@@ -116,9 +124,10 @@ def gather_kv(k_pool, v_pool, block_table_row, n_tokens: int, H_kv: int, D: int)
         z = np.zeros((0, H_kv, D), dtype=np.float64)
         return z, z.copy()
     blocks = np.asarray(block_table_row[:nblk], dtype=np.int64)
-    kt = k_pool[blocks].reshape(nblk, H_kv, BLOCK, D)            # (blk, h, o, d)
+    W = k_group(D)
+    kt = k_pool[blocks].reshape(nblk, H_kv, D // W, BLOCK, W)   # (blk, h, group, o, d % W)
     vt = v_pool[blocks].reshape(nblk, H_kv, D, BLOCK)            # (blk, h, d, o)
-    K = kt.transpose(0, 2, 1, 3).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
+    K = kt.transpose(0, 3, 1, 2, 4).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
     V = vt.transpose(0, 3, 1, 2).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
     return bf16_bits_to_f64(K), bf16_bits_to_f64(V)
 
@@ -148,8 +157,9 @@ def pools_after_append(k_pool, v_pool, slots, k_new, v_new):
         if x < 0:
             continue
         b, o = divmod(x, BLOCK)
+        W = k_group(D)
         for h in range(H_kv):
-            k_out[b, h, o * D:(o + 1) * D] = k_new[t, h]
+            k_out[b, h].reshape(D // W, BLOCK, W)[:, o, :] = np.asarray(k_new[t, h]).reshape(D // W, W)
             v_out[b, h, o::BLOCK][:D] = v_new[t, h]
     return k_out, v_out
 

@@ -24,8 +24,9 @@
 // eight C values are keys 8g .. 8g+7 of the step, exactly the slots it needs
 // as the B operand (P^T) of the P.V product.  The V tile of a block is
 // stored dimension-major (16 tokens contiguous per dimension), so the V^T A
-// operand is one 16-byte load per lane; K tiles are token-major and the K A
-// operand is one 16-byte load per lane per 32 dimensions.  Narrow items load
+// operand is one 16-byte load per lane; K tiles hold 32-dimension groups,
+// each token-major, so the K A operand is one 16-byte load per lane per 32
+// dimensions and every load reads whole cache lines.  Narrow items load
 // their operands straight from HBM in MFMA layout; wide tiles stage each
 // chunk once per workgroup in LDS, in the same layout.
 #include <hip/hip_runtime.h>
@@ -48,6 +49,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = pkv::kHeadDim;
 constexpr int TILE = pkv::kBlock * pkv::kHeadDim;  // elements of a (block, head) tile
+// K tiles hold the dimensions in groups of 32, each group token-major: a
+// 16-byte load per lane over 16 keys x 32 dimensions reads whole cache
+// lines (one 32-dimension MFMA step of 16 keys is 1 KiB contiguous).
+constexpr int kKGroup = 32;
+constexpr int kKGroupElems = pkv::kBlock * kKGroup;
 
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -137,9 +143,9 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
 
 // ---------------------------------------------------------------------------
 // append: a workgroup per 16 consecutive packed rows and one kv head, a
-// thread per (row, 8 dimensions) for K and for V.  K rows are token-major in
-// the cache: lanes run over dimensions, each row's 256 bytes are one
-// contiguous store.  V tiles are dimension-major (a block's 16 tokens
+// thread per (row, 8 dimensions) for K and for V.  K rows: lanes run over
+// dimensions, each row's 256 bytes are four 64-byte stores, one per
+// 32-dimension group of the tile.  V tiles are dimension-major (a block's 16 tokens
 // contiguous per dimension): lanes run over rows, so each 2-byte store
 // instruction writes, per dimension, the consecutive slots of up to 16
 // consecutive rows -- whole sectors inside any prefill run, whatever its
@@ -178,7 +184,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int64_t sl = srow[i];
     if (t0 + i < T && sl >= 0) {
       const u32x4 x = load16(k_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
-      *reinterpret_cast<u32x4 *>(kc + ((sl >> 4) * Hkv + h) * TILE + (sl & 15) * D + d0) = x;
+      *reinterpret_cast<u32x4 *>(kc + ((sl >> 4) * Hkv + h) * TILE + (d0 / kKGroup) * kKGroupElems +
+                                 (sl & 15) * kKGroup + d0 % kKGroup) = x;
     }
   }
   {  // V: lanes over rows
@@ -287,7 +294,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
   // per-lane constant parts of the operand addresses
   const int ka = r >> 2, kbb = r & 3;               // K row r -> key 8*ka + 4*mt + kbb
   const int k_sel = ka >> 1;                         // which block of the pair
-  const int k_row_off = (8 * (ka & 1) + kbb) * D + 8 * g;  // + 4*mt*D + 32*c
+  const int k_row_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g;  // + 4*mt*kKGroup + c*kKGroupElems
   const int v_sel = g >> 1;
   const int v_off = r * pkv::kBlock + 8 * (g & 1);         // + 16*dt*16
 
@@ -310,7 +317,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * D + 32 * c);
+      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * kKGroup + c * kKGroupElems);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * pkv::kBlock);
     ch.bad0 = !ok0;
@@ -589,9 +596,9 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
   {
     const int ka = r >> 2, kbb = r & 3;
     const int R0 = w * RPW;
-    if (kside) {  // region R: m-tile R/4 (keys +4), 32-dim step R%4
+    if (kside) {  // region R: m-tile R/4 (keys +4), 32-dim group R%4
       sel = ka >> 1;
-      lane_off = (8 * (ka & 1) + kbb) * D + 8 * g + 4 * (R0 >> 2) * D + 32 * (R0 & 3);
+      lane_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g + 4 * (R0 >> 2) * kKGroup + (R0 & 3) * kKGroupElems;
     } else {      // region R: 16-dim tile R-8
       sel = g >> 1;
       lane_off = r * pkv::kBlock + 8 * (g & 1) + (R0 - 8) * 16 * pkv::kBlock;
@@ -627,7 +634,8 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     const uint16_t *src = (sel ? tile(b1) : tile(b0)) + lane_off;
     u32x4 *dst = slot(n_issued) + w * RPW * 64;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src + (kside ? 32 : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + (kside ? kKGroupElems : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0,
+                                     0);
     ++n_issued;
     if (ci < i1 && ++ccc >= cd.nch) {
       ccc = 0;

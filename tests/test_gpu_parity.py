@@ -78,10 +78,11 @@ def check_append(batch, slots, t, blocks=None):
     v_exp = np.asarray(batch.v_pool[touched]).copy()
     pos = {int(b): i for i, b in enumerate(touched)}
     D = batch.head_dim
+    W = oracle.k_group(D)
     for row, x in enumerate(ref_slots):
         b, o = divmod(int(x), 16)
         for h in range(batch.num_kv_heads):
-            k_exp[pos[b], h, o * D:(o + 1) * D] = batch.k_new[row, h]
+            k_exp[pos[b], h].reshape(D // W, 16, W)[:, o, :] = batch.k_new[row, h].reshape(D // W, W)
             v_exp[pos[b], h, o::16][:D] = batch.v_new[row, h]
     assert np.array_equal(k_dev.reshape(k_exp.shape), k_exp)
     assert np.array_equal(v_dev.reshape(v_exp.shape), v_exp)
@@ -239,8 +240,9 @@ def test_nan_in_unused_slots_does_not_leak(dev):
     for s in range(b.num_seqs):
         n = int(b.seq_lens[s])
         last = int(b.block_tables[s, (n - 1) // 16])
+        W = oracle.k_group(D)
         for o in range(n % 16 or 16, 16):
-            b.k_pool[last, :, o * D:(o + 1) * D] = 0x7FC0
+            b.k_pool[last].reshape(b.num_kv_heads, D // W, 16, W)[:, :, o, :] = 0x7FC0
             b.v_pool[last, :, o::16] = 0x7FC0
     out, _, _, _ = run_step(b, dev)
     check_attention(out, oracle.packed_attention(b), "nan tails")
@@ -259,10 +261,11 @@ def test_growing_scores_recompute(dev):
     b.q[:] = one
     kval = lambda p: wl.f32_to_bf16_bits(np.float32(0.125 * (p // 32)))
     cu = b.cu_seqlens_q
+    W = oracle.k_group(D)
     for s, (c, ql) in enumerate(seqs):
         for p in range(c):
             blk = int(b.block_tables[s, p // 16])
-            b.k_pool[blk, :, (p % 16) * D:(p % 16 + 1) * D] = kval(p)
+            b.k_pool[blk].reshape(b.num_kv_heads, D // W, 16, W)[:, :, p % 16, :] = kval(p)
         for j in range(ql):
             b.k_new[cu[s] + j] = kval(c + j)
     note("growing scores")

@@ -91,6 +91,16 @@ def test_pins_catch_wrong_v_tile_reading(monkeypatch):
         pins.test_gather_blockwise_equals_token_by_token()
 
 
+def test_pins_catch_token_major_k_reading(monkeypatch):
+    def token_major_k(k_pool, slot, head, D):
+        b, o = divmod(int(slot), 16)
+        return k_pool[b, head][o * D:(o + 1) * D]
+
+    monkeypatch.setattr(pa, "read_k_token", token_major_k)
+    with pytest.raises(AssertionError):
+        pins.test_gather_grouped_k_tiles()
+
+
 def test_pins_catch_wrong_slot_offset(monkeypatch):
     def bad_slot(row, pos):
         return int(row[pos // 16]) * 16 + (pos % 16 + 1) % 16

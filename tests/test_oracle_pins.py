@@ -111,6 +111,23 @@ def test_gather_blockwise_equals_token_by_token():
         assert np.array_equal(K1, K2) and np.array_equal(V1, V2)
 
 
+def test_gather_grouped_k_tiles():
+    """D = 64: two 32-dimension groups per K tile.  The block-wise gather
+    equals the token-by-token reads, and token o's dimensions 32..63 sit in
+    the second group at o * 32 (written out by hand for one token)."""
+    b = small_batch([(37, 2), (0, 5)], D=64, pool="materialize")
+    for s in range(b.num_seqs):
+        n = int(b.seq_lens[s])
+        K1, V1 = pa.gather_kv(b.k_pool, b.v_pool, b.block_tables[s], n, 2, 64)
+        K2, V2 = pa.gather_kv_by_token(b.k_pool, b.v_pool, b.block_tables[s], n, 2, 64)
+        assert np.array_equal(K1, K2) and np.array_equal(V1, V2)
+    blk, o, h = int(b.block_tables[0, 1]), 5, 1          # position 21 of sequence 0
+    tile = b.k_pool[blk, h]
+    by_hand = np.concatenate([tile[o * 32:(o + 1) * 32], tile[512 + o * 32:512 + (o + 1) * 32]])
+    K, _ = pa.gather_kv(b.k_pool, b.v_pool, b.block_tables[0], 37, 2, 64)
+    assert np.array_equal(K[21, h], oracle.bf16_bits_to_f64(by_hand))
+
+
 def test_append_round_trip_and_untouched_tiles():
     b = small_batch([(37, 3), (15, 1), (0, 16)], D=16, unused_fill="normal", pool="materialize")
     slots = oracle.slot_mapping(b.cu_seqlens_q, b.seq_lens, b.block_tables)
