@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace"])
+    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap"])
     p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
     p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,6 +146,9 @@ def main():
         sys.exit(1)
     if args.workload == "trace":
         run_trace(args)
+        return
+    if args.workload in ("blockcopy", "swap"):
+        run_blocks(args)
         return
     dev = torch.device("cuda", 0)
     pkv.load_library()
@@ -334,6 +337,74 @@ def run_trace(args):
                           "ms": round(float(ms[pre].sum()), 3) if pre.any() else None},
         "per_step_ms_first": [round(float(x), 3) for x in ms[:8]],
     }
+    print(json.dumps(res), flush=True)
+
+
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def run_blocks(args):
+    """Whole-block moves on one synthetic 16,384-block pool (8 kv heads,
+    head_dim 128: 64 KiB of K and V per block): copy-on-write copies of 4,096
+    disjoint random (src, dst) pairs in HBM, or a swap of 2,048 random blocks
+    to pinned host memory and back.  K launches after W warm-ups, HIP events
+    on the stream."""
+    import torch
+    import paged_kv_cache_149_amd as pkv
+    dev = torch.device("cuda", 0)
+    pkv.load_library()
+    Hkv, D, nb = 8, 128, 16384
+    kc = torch.empty(nb, Hkv, 16, D, dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty(nb, Hkv, D, 16, dtype=torch.bfloat16, device=dev).normal_()
+    perm = np.random.default_rng(149100).permutation(nb).astype(np.int32)
+    blk = 2 * Hkv * 16 * D * 2
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, k):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if args.workload == "blockcopy":
+        n = 4096
+        pairs = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).copy()).to(dev)
+        ms = timed(lambda: pkv.pkv_copy_blocks(kc, vc, pairs), args.steps)
+        moved = 2 * n * blk
+        gbs = moved / (ms * 1e-3) / 1e9
+        res = {"metric": "kv block copy-on-write: GB/s moved vs HBM roofline, 1 GPU", "value": round(gbs, 1),
+               "unit": "GB/s", "ms_per_step": round(ms, 5), **base,
+               "config": {"workload": f"blockcopy-{n}pairs-{Hkv}kv-pool{nb}", "pairs": n, "block_bytes": blk},
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "copy_blocks_kernel", "bytes_per_launch": moved}}
+    else:
+        n = 2048
+        blocks = torch.from_numpy(perm[:n].copy()).to(dev)
+        host = torch.empty(pkv.swap_bytes(Hkv, n) // 2, dtype=torch.int16, pin_memory=True)
+        ms_out = timed(lambda: pkv.pkv_swap_out(kc, vc, blocks, host), args.steps)
+        ms_in = timed(lambda: pkv.pkv_swap_in(host, blocks, kc, vc), args.steps)
+        nbytes = n * blk
+        out_gbs, in_gbs = nbytes / (ms_out * 1e-3) / 1e9, nbytes / (ms_in * 1e-3) / 1e9
+        rt = 2 * nbytes / ((ms_out + ms_in) * 1e-3) / 1e9
+        # an 8,192-token context over 32 layers at 4 KiB per token per layer
+        ctx = 8192 * 32 * 4096
+        res = {"metric": "kv swap to pinned host memory: GB/s per direction vs PCIe, 1 GPU", "value": round(rt, 1),
+               "unit": "GB/s", "ms_per_step": round(ms_out + ms_in, 5), **base,
+               "config": {"workload": f"swap-{n}blocks-{Hkv}kv-pool{nb}", "blocks": n, "bytes_each_way": nbytes},
+               "out_GBs": round(out_gbs, 1), "in_GBs": round(in_gbs, 1),
+               "ms_8k_context_32_layers_round_trip": round(ctx / (out_gbs * 1e9) * 1e3 + ctx / (in_gbs * 1e9) * 1e3, 2),
+               "roofline": {"bound": "pcie", "achieved": round(rt, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(rt / PCIE_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "swap_kernel", "bytes_per_launch": nbytes}}
     print(json.dumps(res), flush=True)
 
 

@@ -261,6 +261,89 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
                    void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream);
 
+/* ===========================================================================
+ * Block pool, copy-on-write and swap (the steps either side of the append).
+ * ======================================================================== */
+
+/* ---------------------------------------------------------------------------
+ * Host block pool ("连续批处理与 PagedAttention 原理", section "块管理器": the
+ * physical block pool records which blocks are free and a reference count
+ * per block in use; its operations are allocate, free and copy-on-write.
+ * "11.2 连续批处理与 PagedAttention", section 11.2.3 "共享": several logical
+ * blocks may map to one physical block; when the output sequences of one
+ * request share the prompt's blocks, only a shared block that is not yet
+ * full is copied before a sequence writes into it; shared full prefix
+ * blocks are read-only and need no copy).
+ *
+ * Host memory only; no GPU call.  Free blocks form a stack: allocation pops
+ * the top, a block whose count drops to zero is pushed on top, and a new pool
+ * has block 0 on top, then 1, 2, ...  Not thread-safe: one pool, one thread
+ * at a time.  Errors: PKV_EINVAL (null pointer, negative size, a table row
+ * naming a block not in use), PKV_ERANGE (not enough free blocks, an id
+ * outside the pool, more releases than references).  A call that fails
+ * changes nothing.
+ * ------------------------------------------------------------------------- */
+typedef struct pkv_block_pool pkv_block_pool_t;
+
+int pkv_block_pool_create(int64_t num_blocks, pkv_block_pool_t **pool);
+void pkv_block_pool_destroy(pkv_block_pool_t *pool);
+/* free blocks (-1 for a null pool) */
+int64_t pkv_block_pool_num_free(const pkv_block_pool_t *pool);
+/* references to `block` (0 = free; -1 for an id outside the pool) */
+int32_t pkv_block_pool_refcount(const pkv_block_pool_t *pool, int32_t block);
+/* n blocks, each with one reference, written to h_blocks[0..n) */
+int pkv_block_pool_allocate(pkv_block_pool_t *pool, int32_t n, int32_t *h_blocks);
+/* one more reference to each listed block (a forked sequence, or a prefix
+ * reused by another request, maps the same physical blocks) */
+int pkv_block_pool_share(pkv_block_pool_t *pool, const int32_t *h_blocks, int32_t n);
+/* one reference fewer to each listed block (repeats count); blocks that
+ * reach zero become free */
+int pkv_block_pool_release(pkv_block_pool_t *pool, const int32_t *h_blocks, int32_t n);
+/* Prepare a sequence's block-table row (h_table_row, `capacity` entries)
+ * for writing num_new tokens after its num_tokens: if the block that
+ * position num_tokens falls in is already held and has more than one
+ * reference, it is replaced in the row by a newly allocated block, the old
+ * one loses this reference, and the pair (old, new) is written to
+ * h_copies[0..2) (*num_copies = 1): the caller copies old -> new on the
+ * device (pkv_copy_blocks) before appending.  Then every further block the
+ * new tokens need is allocated into the row.  *num_copies = 0 when nothing
+ * is to be copied (h_copies may then be NULL). */
+int pkv_block_pool_append_slots(pkv_block_pool_t *pool, int32_t *h_table_row, int32_t capacity,
+                                int32_t num_tokens, int32_t num_new, int32_t *h_copies,
+                                int32_t *num_copies);
+
+/* ---------------------------------------------------------------------------
+ * Copy-on-write on the device: for p in [0, num_pairs), block
+ * block_pairs[2p] is copied bit for bit onto block block_pairs[2p + 1], K
+ * and V, every kv head (block_pairs: device int32[num_pairs][2]).  Pairs
+ * with an id outside [0, num_blocks) or src == dst are skipped; two pairs
+ * with the same destination, or a destination that is another pair's
+ * source, race (undefined).  Errors as for pkv_paged_kv_append.
+ * ------------------------------------------------------------------------- */
+int pkv_copy_blocks(pkv_bf16 *k_cache, pkv_bf16 *v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                    int32_t head_dim, const int32_t *block_pairs, int32_t num_pairs, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Swap preemption ("连续批处理与 PagedAttention 原理", section "抢占策略": the
+ * KV cache of a preempted sequence is copied to CPU memory and copied back
+ * when it resumes, at the cost of PCIe bandwidth and host memory;
+ * "Continuous Batching 深入实现", section "Preemption 与 Recompute vs Swap").
+ * pkv_swap_out copies blocks[p] (device int32[num]) of both pools into
+ * host_dst + p * 2 * S, K first, then V, where S = num_kv_heads * 16 * 128
+ * bf16 elements is one block of one pool, in the pools' own tile layout;
+ * pkv_swap_in copies them back into blocks[p].  The host buffer must be
+ * page-locked, device-mapped host memory (hipHostMalloc, or a pinned torch
+ * tensor) of at least num * 2 * S * 2 bytes; the kernels read or write it
+ * directly.  Ids outside [0, num_blocks) are skipped (their host slot is
+ * left untouched on the way out and ignored on the way in).  Errors as for
+ * pkv_paged_kv_append; PKV_EINVAL also for a host buffer that is not
+ * device-mapped.
+ * ------------------------------------------------------------------------- */
+int pkv_swap_out(const pkv_bf16 *k_cache, const pkv_bf16 *v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                 int32_t head_dim, const int32_t *blocks, int32_t num, void *host_dst, pkv_stream_t stream);
+int pkv_swap_in(const void *host_src, const int32_t *blocks, int32_t num, pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim, pkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,7 @@ HIP sources in csrc/; this package is its thin Python binding.
 
 from .binding import (  # noqa: F401
     BLOCK_SIZE,
+    BlockPool,
     HEAD_DIM,
     PKVError,
     Plan,
@@ -13,12 +14,16 @@ from .binding import (  # noqa: F401
     bf16_tensor,
     header_functions,
     load_library,
+    pkv_copy_blocks,
     pkv_paged_kv_append,
     pkv_paged_step,
     pkv_paged_varlen_attention,
     pkv_plan,
     pkv_slot_append,
     pkv_slot_mapping,
+    swap_bytes,
     pkv_split_kv_reduce,
+    pkv_swap_in,
+    pkv_swap_out,
     pkv_varlen_attention_main,
 )

@@ -80,6 +80,17 @@ _SIGNATURES = {
                                                   ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
     "pkv_paged_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
                                       ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_block_pool_create": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
+    "pkv_block_pool_destroy": (None, [_P]),
+    "pkv_block_pool_num_free": (_I64, [_P]),
+    "pkv_block_pool_refcount": (_I32, [_P, _I32]),
+    "pkv_block_pool_allocate": (ctypes.c_int, [_P, _I32, _P]),
+    "pkv_block_pool_share": (ctypes.c_int, [_P, _P, _I32]),
+    "pkv_block_pool_release": (ctypes.c_int, [_P, _P, _I32]),
+    "pkv_block_pool_append_slots": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, ctypes.POINTER(_I32)]),
+    "pkv_copy_blocks": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _I32, _P]),
+    "pkv_swap_out": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _I32, _P, _P]),
+    "pkv_swap_in": (ctypes.c_int, [_P, _P, _I32, _P, _P, _I64, _I32, _I32, _P]),
 }
 
 _lib = None
@@ -357,3 +368,116 @@ def pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, bl
         _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], nb, _ptr(slot_mapping),
         float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
     return out, slot_mapping
+
+
+# ---------------------------------------------------------------------------
+# block pool, copy-on-write and swap
+# ---------------------------------------------------------------------------
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+class BlockPool:
+    """The library's host block pool (reference counts, a stack of free
+    blocks, copy-on-write of a shared partial block before an append)."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check("pkv_block_pool_create", self._lib.pkv_block_pool_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_block_pool_destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_block_pool_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_block_pool_refcount(self._h, int(block)))
+
+    def allocate(self, n: int) -> np.ndarray:
+        out = np.empty(int(n), dtype=np.int32)
+        _check("pkv_block_pool_allocate", self._lib.pkv_block_pool_allocate(
+            self._h, int(n), out.ctypes.data_as(_P)))
+        return out
+
+    def share(self, blocks) -> None:
+        b = _i32(blocks)
+        _check("pkv_block_pool_share", self._lib.pkv_block_pool_share(self._h, b.ctypes.data_as(_P), b.size))
+
+    def release(self, blocks) -> None:
+        b = _i32(blocks)
+        _check("pkv_block_pool_release", self._lib.pkv_block_pool_release(self._h, b.ctypes.data_as(_P), b.size))
+
+    def append_slots(self, row: np.ndarray, num_tokens: int, num_new: int):
+        """Prepare a block-table row (int32, modified in place) for num_new
+        tokens after num_tokens; returns the (src, dst) copy to make first,
+        or None."""
+        if row.dtype != np.int32 or not row.flags.c_contiguous:
+            raise TypeError("row must be a contiguous int32 array")
+        copies = np.empty(2, dtype=np.int32)
+        n = _I32()
+        _check("pkv_block_pool_append_slots", self._lib.pkv_block_pool_append_slots(
+            self._h, row.ctypes.data_as(_P), row.size, int(num_tokens), int(num_new),
+            copies.ctypes.data_as(_P), ctypes.byref(n)))
+        return (int(copies[0]), int(copies[1])) if n.value else None
+
+
+def _pool_shapes(k_cache, v_cache):
+    nb, Hkv, _, D = k_cache.shape
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    return nb, Hkv, D
+
+
+def pkv_copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """Copy block pairs[p, 0] onto pairs[p, 1] in both pools (device int32 [n, 2])."""
+    lib = load_library()
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(pairs, "pairs", torch.int32, dev)
+    nb, Hkv, D = _pool_shapes(k_cache, v_cache)
+    n = pairs.shape[0] if pairs.numel() else 0
+    _check("pkv_copy_blocks", lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), nb, Hkv, D, _ptr(pairs), n,
+                                                  _stream(stream, dev)))
+
+
+def swap_bytes(num_kv_heads: int, num: int, head_dim: int = HEAD_DIM) -> int:
+    """Host bytes that num swapped blocks take (K and V)."""
+    return int(num) * 2 * num_kv_heads * BLOCK_SIZE * head_dim * 2
+
+
+def pkv_swap_out(k_cache, v_cache, blocks, host, stream=None):
+    """Copy the listed blocks (device int32) into the pinned host tensor."""
+    lib = load_library()
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(blocks, "blocks", torch.int32, dev)
+    nb, Hkv, D = _pool_shapes(k_cache, v_cache)
+    if not host.is_pinned() or host.numel() * host.element_size() < swap_bytes(Hkv, blocks.numel(), D):
+        raise ValueError("host must be a pinned tensor of at least swap_bytes() bytes")
+    _check("pkv_swap_out", lib.pkv_swap_out(_ptr(k_cache), _ptr(v_cache), nb, Hkv, D, _ptr(blocks),
+                                            blocks.numel(), _ptr(host), _stream(stream, dev)))
+
+
+def pkv_swap_in(host, blocks, k_cache, v_cache, stream=None):
+    """Copy the pinned host tensor's blocks back into the listed blocks."""
+    lib = load_library()
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(blocks, "blocks", torch.int32, dev)
+    nb, Hkv, D = _pool_shapes(k_cache, v_cache)
+    if not host.is_pinned() or host.numel() * host.element_size() < swap_bytes(Hkv, blocks.numel(), D):
+        raise ValueError("host must be a pinned tensor of at least swap_bytes() bytes")
+    _check("pkv_swap_in", lib.pkv_swap_in(_ptr(host), _ptr(blocks), blocks.numel(), _ptr(k_cache),
+                                          _ptr(v_cache), nb, Hkv, D, _stream(stream, dev)))

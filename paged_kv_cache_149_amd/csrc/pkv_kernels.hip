@@ -959,6 +959,59 @@ __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(A
 }
 
 // ---------------------------------------------------------------------------
+// whole-block copies and host swaps: a workgroup per (listed block, K or V);
+// 256 threads move the block's num_kv_heads tiles (4 KiB each) with 16-byte
+// loads and stores, eight in flight per thread.  Ids outside [0, num_blocks)
+// are skipped.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void copy_slab(const u32x4 *__restrict__ s, u32x4 *__restrict__ d, int nvec) {
+  for (int i0 = 0; i0 < nvec; i0 += 256 * 8) {
+    u32x4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      if (i < nvec) x[u] = __builtin_nontemporal_load(s + i);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + (int)threadIdx.x;
+      if (i < nvec) __builtin_nontemporal_store(x[u], d + i);
+    }
+  }
+}
+
+// pairs[2p] -> pairs[2p + 1]
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint16_t *kc, uint16_t *vc, const int32_t *__restrict__ pairs,
+                                                          int32_t n, int64_t num_blocks, int32_t Hkv) {
+  const int p = blockIdx.x;
+  if (p >= n) return;
+  const int64_t src = sload(pairs, 2 * (int64_t)p), dst = sload(pairs, 2 * (int64_t)p + 1);
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  uint16_t *base = blockIdx.y ? vc : kc;
+  const int64_t slab = (int64_t)Hkv * TILE;
+  copy_slab(reinterpret_cast<const u32x4 *>(base + src * slab), reinterpret_cast<u32x4 *>(base + dst * slab),
+            (int)(slab / 8));
+}
+
+// host[p][side][Hkv * TILE] <-> block blocks[p] of the K (side 0) / V (side 1) pool
+template <bool kOut>
+__global__ __launch_bounds__(256) void swap_kernel(uint16_t *kc, uint16_t *vc, const int32_t *__restrict__ blocks,
+                                                   int32_t n, int64_t num_blocks, int32_t Hkv, uint16_t *host) {
+  const int p = blockIdx.x;
+  if (p >= n) return;
+  const int64_t b = sload(blocks, p);
+  if (b < 0 || b >= num_blocks) return;
+  uint16_t *base = blockIdx.y ? vc : kc;
+  const int64_t slab = (int64_t)Hkv * TILE;
+  uint16_t *dev = base + b * slab;
+  uint16_t *hst = host + ((int64_t)p * 2 + blockIdx.y) * slab;
+  if (kOut)
+    copy_slab(reinterpret_cast<const u32x4 *>(dev), reinterpret_cast<u32x4 *>(hst), (int)(slab / 8));
+  else
+    copy_slab(reinterpret_cast<const u32x4 *>(hst), reinterpret_cast<u32x4 *>(dev), (int)(slab / 8));
+}
+
+// ---------------------------------------------------------------------------
 // merge of key-split partials: one wavefront per (row, head); lane l owns
 // dimensions 2l, 2l+1
 // ---------------------------------------------------------------------------
@@ -1131,6 +1184,59 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                                      scale, plan, ws, ws_bytes, out, stream);
   if (st != PKV_OK) return st;
   return pkv_split_kv_reduce(plan, ws, ws_bytes, out, stream);
+}
+
+int pkv_copy_blocks(pkv_bf16 *k_cache, pkv_bf16 *v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                    int32_t head_dim, const int32_t *block_pairs, int32_t num_pairs, pkv_stream_t stream) {
+  if (num_pairs < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  if (head_dim != D) return PKV_EUNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PKV_EINVAL;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, as_stream(stream), k_cache, v_cache,
+                     block_pairs, num_pairs, num_blocks, num_kv_heads);
+  return launch_status();
+}
+
+namespace {
+// the device address of a pinned (page-locked, device-mapped) host buffer
+int device_view(void *host, uint16_t **dev) {
+  void *d = nullptr;
+  if (!host || hipHostGetDevicePointer(&d, host, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return PKV_EINVAL;
+  }
+  *dev = static_cast<uint16_t *>(d);
+  return PKV_OK;
+}
+}  // namespace
+
+int pkv_swap_out(const pkv_bf16 *k_cache, const pkv_bf16 *v_cache, int64_t num_blocks, int32_t num_kv_heads,
+                 int32_t head_dim, const int32_t *blocks, int32_t num, void *host_dst, pkv_stream_t stream) {
+  if (num < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  if (head_dim != D) return PKV_EUNSUPPORTED;
+  if (num == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !blocks) return PKV_EINVAL;
+  uint16_t *hst;
+  const int st = device_view(host_dst, &hst);
+  if (st != PKV_OK) return st;
+  hipLaunchKernelGGL(swap_kernel<true>, dim3(num, 2), dim3(256), 0, as_stream(stream),
+                     const_cast<uint16_t *>(k_cache), const_cast<uint16_t *>(v_cache), blocks, num, num_blocks,
+                     num_kv_heads, hst);
+  return launch_status();
+}
+
+int pkv_swap_in(const void *host_src, const int32_t *blocks, int32_t num, pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim, pkv_stream_t stream) {
+  if (num < 0 || num_blocks < 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  if (head_dim != D) return PKV_EUNSUPPORTED;
+  if (num == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !blocks) return PKV_EINVAL;
+  uint16_t *hst;
+  const int st = device_view(const_cast<void *>(host_src), &hst);
+  if (st != PKV_OK) return st;
+  hipLaunchKernelGGL(swap_kernel<false>, dim3(num, 2), dim3(256), 0, as_stream(stream), k_cache, v_cache, blocks,
+                     num, num_blocks, num_kv_heads, hst);
+  return launch_status();
 }
 
 int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t *cu_seqlens_q,
