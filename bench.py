@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap"])
+    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap", "prefixcache"])
     p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
     p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,6 +149,9 @@ def main():
         return
     if args.workload in ("blockcopy", "swap"):
         run_blocks(args)
+        return
+    if args.workload == "prefixcache":
+        run_prefix(args)
         return
     dev = torch.device("cuda", 0)
     pkv.load_library()
@@ -405,6 +408,128 @@ def run_blocks(args):
                "roofline": {"bound": "pcie", "achieved": round(rt, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                             "frac": round(rt / PCIE_PEAK_GBS, 4), "traffic": None,
                             "kernel": "swap_kernel", "bytes_per_launch": nbytes}}
+    print(json.dumps(res), flush=True)
+
+
+def run_prefix(args):
+    """Prefix caching on the worked example of 11.2.4, sixteen times over: 16
+    requests share a 2,010-token prompt and add 200 tokens each (8 kv heads,
+    32 query heads, head_dim 128).  Cold: no cache, all 16 prefill their
+    2,210 tokens in one packed step.  Warm: an earlier request registered
+    the prompt; each request hits 125 blocks (2,000 tokens) in the library's
+    pool and its step prefills 210 rows against 2,210 keys.  Both steps are
+    append + attention + merge, timed as in the main workload; the host
+    pool work (match, allocate, register) is timed on its own: it runs once
+    per request, while the step runs once per layer.  `value` is prompt
+    tokens (cached + computed) per second of the warm step."""
+    import torch
+    import paged_kv_cache_149_amd as pkv
+    from paged_kv_cache_149_amd import accounting
+    dev = torch.device("cuda", 0)
+    pkv.load_library()
+    R, shared_n, own_n, Hq, Hkv, D = 16, 2010, 200, 32, 8, 128
+    total = shared_n + own_n
+    rng = np.random.default_rng(149200)
+    shared = rng.integers(0, 50000, size=shared_n, dtype=np.int32)
+    prompts = [np.concatenate([shared, rng.integers(0, 50000, size=own_n, dtype=np.int32)]) for _ in range(R + 1)]
+    nb = (R + 1) * 140
+    pool = pkv.BlockPool(nb)
+    cap = 140
+    kc = torch.empty(nb, Hkv, 16, D, dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty(nb, Hkv, D, 16, dtype=torch.bfloat16, device=dev).normal_()
+    stream = torch.cuda.current_stream(dev)
+    scale = 1.0 / np.sqrt(D)
+
+    # the request that fills the cache, then finishes
+    row0 = np.full(cap, -1, np.int32)
+    pool.append_slots(row0, 0, total)
+    pool.register_prefix(prompts[0], row0)
+    pool.release(row0[:139][::-1])
+
+    # warm admission: host-side pool work for 16 requests
+    t0 = time.perf_counter()
+    rows_w, cached = [], []
+    for r in range(R):
+        row = np.full(cap, -1, np.int32)
+        c = pool.match_prefix(prompts[r + 1], row)
+        pool.append_slots(row, c, total - c)
+        rows_w.append(row), cached.append(c)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    for r in range(R):
+        pool.register_prefix(prompts[r + 1], rows_w[r])
+    register_ms = (time.perf_counter() - t0) * 1e3
+    assert all(c == 2000 for c in cached)
+    # cold: the same requests, each in blocks of its own
+    cold_pool = pkv.BlockPool(nb)
+    rows_c = []
+    for r in range(R):
+        row = np.full(cap, -1, np.int32)
+        cold_pool.append_slots(row, 0, total)
+        rows_c.append(row)
+
+    def setup(rows, q_len):
+        cu = np.arange(R + 1, dtype=np.int32) * q_len
+        sl = np.full(R, total, np.int32)
+        bt = np.stack(rows)
+        T = int(cu[-1])
+        g = torch.Generator(device=dev).manual_seed(149201)
+        mk = lambda h: torch.randn(T, h, D, device=dev, generator=g).to(torch.bfloat16)
+        t = {"q": mk(Hq), "k_new": mk(Hkv), "v_new": mk(Hkv), "cu": torch.from_numpy(cu).to(dev),
+             "sl": torch.from_numpy(sl).to(dev), "bt": torch.from_numpy(bt).to(dev)}
+        plan = pkv.pkv_plan(cu, sl, Hq, Hkv, D, block_tables=bt, num_blocks=nb, device=dev, stream=stream)
+        return cu, sl, bt, t, plan
+
+    def timed(cu, sl, bt, t, plan):
+        slots = torch.empty(t["q"].shape[0], dtype=torch.int64, device=dev)
+        out = torch.empty_like(t["q"])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+
+        def step(i=None):
+            pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu"], t["sl"], t["bt"], kc, vc,
+                                slot_mapping=slots, stream=stream)
+            if i is not None:
+                ev[i][0].record(stream)
+            pkv.pkv_varlen_attention_main(t["q"], kc, vc, t["bt"], scale, plan, out=out, stream=stream)
+            if i is not None:
+                ev[i][1].record(stream)
+            pkv.pkv_split_kv_reduce(plan, out, stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - a) * 1e3 / args.steps
+        attn = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+        flop = accounting.attention_flop(cu, sl, Hq, D)
+        return ms, attn, flop
+
+    log("prefix cache: cold step, 16 x 2210 rows")
+    cold_ms, cold_attn, cold_flop = timed(*setup(rows_c, total))
+    log("prefix cache: warm step, 16 x 210 rows over 2210 keys")
+    warm_ms, warm_attn, warm_flop = timed(*setup(rows_w, total - 2000))
+    tflops = warm_flop / (warm_attn * 1e-3) / 1e12
+    res = {"metric": "prefix-cached prefill step: prompt tokens served per second, 1 GPU",
+           "value": round(R * total / (warm_ms * 1e-3), 1), "unit": "tok/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(warm_ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"prefix-{R}req-{shared_n}shared-{own_n}own", "requests": R,
+                      "cached_tokens_each": 2000, "rows_each_warm": total - 2000, "keys_each": total},
+           "cold_ms_per_step": round(cold_ms, 5), "cold_tok_s": round(R * total / (cold_ms * 1e-3), 1),
+           "warm_over_cold_step": round(warm_ms / cold_ms, 4),
+           "rows_fraction": round((total - 2000) / total, 4),
+           "host_us_per_request": {"match_and_allocate": round(host_ms * 1e3 / R, 2),
+                                   "register": round(register_ms * 1e3 / R, 2)},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "attention (warm step)", "avg_ms": round(warm_attn, 5),
+                        "flop_per_launch": warm_flop, "cold_avg_ms": round(cold_attn, 5),
+                        "cold_TFLOPs": round(cold_flop / (cold_attn * 1e-3) / 1e12, 2)}}
     print(json.dumps(res), flush=True)
 
 

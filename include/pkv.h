@@ -287,8 +287,11 @@ typedef struct pkv_block_pool pkv_block_pool_t;
 
 int pkv_block_pool_create(int64_t num_blocks, pkv_block_pool_t **pool);
 void pkv_block_pool_destroy(pkv_block_pool_t *pool);
-/* free blocks (-1 for a null pool) */
+/* blocks an allocation can take: free ones plus evictable cached ones (-1
+ * for a null pool) */
 int64_t pkv_block_pool_num_free(const pkv_block_pool_t *pool);
+/* registered prefix blocks, in use or evictable (-1 for a null pool) */
+int64_t pkv_block_pool_num_cached(const pkv_block_pool_t *pool);
 /* references to `block` (0 = free; -1 for an id outside the pool) */
 int32_t pkv_block_pool_refcount(const pkv_block_pool_t *pool, int32_t block);
 /* n blocks, each with one reference, written to h_blocks[0..n) */
@@ -297,7 +300,8 @@ int pkv_block_pool_allocate(pkv_block_pool_t *pool, int32_t n, int32_t *h_blocks
  * reused by another request, maps the same physical blocks) */
 int pkv_block_pool_share(pkv_block_pool_t *pool, const int32_t *h_blocks, int32_t n);
 /* one reference fewer to each listed block (repeats count); blocks that
- * reach zero become free */
+ * reach zero become free, or evictable (queued in the order listed) if
+ * registered as a prefix block */
 int pkv_block_pool_release(pkv_block_pool_t *pool, const int32_t *h_blocks, int32_t n);
 /* Prepare a sequence's block-table row (h_table_row, `capacity` entries)
  * for writing num_new tokens after its num_tokens: if the block that
@@ -311,6 +315,51 @@ int pkv_block_pool_release(pkv_block_pool_t *pool, const int32_t *h_blocks, int3
 int pkv_block_pool_append_slots(pkv_block_pool_t *pool, int32_t *h_table_row, int32_t capacity,
                                 int32_t num_tokens, int32_t num_new, int32_t *h_copies,
                                 int32_t *num_copies);
+
+/* ---------------------------------------------------------------------------
+ * Prefix caching ("11.2 连续批处理与 PagedAttention", section 11.2.4: every
+ * full block gets a hash computed from its parent block's hash, its own
+ * tokens and extra keys; the blocks of a finished request stay in an
+ * evictable queue until a new request hits them or they are pushed out; a
+ * reuse needs a token-exact match, and the key must also carry whatever
+ * changes the KV or its visibility -- model and version, adapter,
+ * multimodal content hash, tenant salt -- here folded by the caller into
+ * one 64-bit extra_key).
+ *
+ * pkv_block_hash: FNV-1a, 64 bits (offset basis 0xcbf29ce484222325, prime
+ * 0x100000001b3), over the little-endian bytes of parent (8), the block's
+ * 16 token ids h_tokens[0..16) (4 each) and extra_key (8); block 0's parent
+ * is 0.  Returns 0 for a null h_tokens.
+ *
+ * pkv_block_pool_match_prefix: for a prompt h_tokens[0..num_tokens), walks
+ * its full blocks from block 0 -- only blocks that leave at least one
+ * prompt token to compute, at most `capacity` -- and stops at the first
+ * block with no registered entry whose tokens, extra key and parent entry
+ * all equal the prompt's (a hash match alone is not enough).  The matched
+ * blocks are written to h_table_row[0..k), each gains one reference (an
+ * evictable one leaves the queue), and *num_cached_tokens = 16 k: the
+ * caller appends and computes only the tokens after it
+ * (pkv_block_pool_append_slots with num_tokens = 16 k).
+ *
+ * pkv_block_pool_register_prefix: registers the full blocks of a computed
+ * sequence (tokens h_tokens[0..num_tokens), table h_table_row, every full
+ * block in use) from block 0 on; a block already registered for the same
+ * content is kept, an entry under the same hash holding other content is
+ * replaced, and the walk stops at a block registered under another hash.
+ * Registration does not change counts.
+ *
+ * Eviction: allocation takes free blocks first, then the evictable block
+ * that was released longest ago, and drops its registration.  Release a
+ * finished request's blocks last block first so that the head of a prefix,
+ * which every later hit needs, is evicted last.  Errors: PKV_EINVAL for a
+ * null pointer, a negative size or a table entry not in use.
+ * ------------------------------------------------------------------------- */
+uint64_t pkv_block_hash(uint64_t parent, const int32_t *h_tokens, uint64_t extra_key);
+int pkv_block_pool_match_prefix(pkv_block_pool_t *pool, const int32_t *h_tokens, int32_t num_tokens,
+                                uint64_t extra_key, int32_t *h_table_row, int32_t capacity,
+                                int32_t *num_cached_tokens);
+int pkv_block_pool_register_prefix(pkv_block_pool_t *pool, const int32_t *h_tokens, int32_t num_tokens,
+                                   uint64_t extra_key, const int32_t *h_table_row);
 
 /* ---------------------------------------------------------------------------
  * Copy-on-write on the device: for p in [0, num_pairs), block

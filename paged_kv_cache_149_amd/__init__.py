@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     bf16_tensor,
     header_functions,
     load_library,
+    pkv_block_hash,
     pkv_copy_blocks,
     pkv_paged_kv_append,
     pkv_paged_step,

@@ -83,6 +83,10 @@ _SIGNATURES = {
     "pkv_block_pool_create": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "pkv_block_pool_destroy": (None, [_P]),
     "pkv_block_pool_num_free": (_I64, [_P]),
+    "pkv_block_pool_num_cached": (_I64, [_P]),
+    "pkv_block_hash": (ctypes.c_uint64, [ctypes.c_uint64, _P, ctypes.c_uint64]),
+    "pkv_block_pool_match_prefix": (ctypes.c_int, [_P, _P, _I32, ctypes.c_uint64, _P, _I32, ctypes.POINTER(_I32)]),
+    "pkv_block_pool_register_prefix": (ctypes.c_int, [_P, _P, _I32, ctypes.c_uint64, _P]),
     "pkv_block_pool_refcount": (_I32, [_P, _I32]),
     "pkv_block_pool_allocate": (ctypes.c_int, [_P, _I32, _P]),
     "pkv_block_pool_share": (ctypes.c_int, [_P, _P, _I32]),
@@ -380,7 +384,8 @@ def _i32(a) -> np.ndarray:
 
 class BlockPool:
     """The library's host block pool (reference counts, a stack of free
-    blocks, copy-on-write of a shared partial block before an append)."""
+    blocks, copy-on-write of a shared partial block before an append, and a
+    prefix cache of registered full blocks with an evictable queue)."""
 
     def __init__(self, num_blocks: int):
         self._lib = load_library()
@@ -399,8 +404,33 @@ class BlockPool:
     def num_free(self) -> int:
         return int(self._lib.pkv_block_pool_num_free(self._h))
 
+    @property
+    def num_cached(self) -> int:
+        return int(self._lib.pkv_block_pool_num_cached(self._h))
+
     def refcount(self, block: int) -> int:
         return int(self._lib.pkv_block_pool_refcount(self._h, int(block)))
+
+    def match_prefix(self, tokens, row: np.ndarray, extra_key: int = 0) -> int:
+        """Map the prompt's leading registered full blocks into ``row``
+        (int32, modified in place); returns the number of cached tokens."""
+        if row.dtype != np.int32 or not row.flags.c_contiguous:
+            raise TypeError("row must be a contiguous int32 array")
+        t = _i32(tokens)
+        n = _I32()
+        _check("pkv_block_pool_match_prefix", self._lib.pkv_block_pool_match_prefix(
+            self._h, t.ctypes.data_as(_P), t.size, int(extra_key) & (2**64 - 1), row.ctypes.data_as(_P),
+            row.size, ctypes.byref(n)))
+        return int(n.value)
+
+    def register_prefix(self, tokens, row, extra_key: int = 0) -> None:
+        """Register the full blocks of a computed sequence for later hits."""
+        t = _i32(tokens)
+        r = _i32(row)
+        if r.size < t.size // BLOCK_SIZE:
+            raise ValueError("row shorter than the sequence's full blocks")
+        _check("pkv_block_pool_register_prefix", self._lib.pkv_block_pool_register_prefix(
+            self._h, t.ctypes.data_as(_P), t.size, int(extra_key) & (2**64 - 1), r.ctypes.data_as(_P)))
 
     def allocate(self, n: int) -> np.ndarray:
         out = np.empty(int(n), dtype=np.int32)
@@ -428,6 +458,15 @@ class BlockPool:
             self._h, row.ctypes.data_as(_P), row.size, int(num_tokens), int(num_new),
             copies.ctypes.data_as(_P), ctypes.byref(n)))
         return (int(copies[0]), int(copies[1])) if n.value else None
+
+
+def pkv_block_hash(parent: int, tokens16, extra_key: int = 0) -> int:
+    """The library's hash of one full block (16 token ids)."""
+    t = _i32(tokens16)
+    if t.size != BLOCK_SIZE:
+        raise ValueError("a block holds 16 tokens")
+    return int(load_library().pkv_block_hash(int(parent) & (2**64 - 1), t.ctypes.data_as(_P),
+                                              int(extra_key) & (2**64 - 1)))
 
 
 def _pool_shapes(k_cache, v_cache):

@@ -1076,7 +1076,7 @@ const char *pkv_status_string(int status) {
   }
 }
 
-int pkv_version(void) { return 102; }
+int pkv_version(void) { return 103; }
 
 int pkv_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                      const int32_t *block_tables, int32_t bt_stride, int32_t num_seqs,

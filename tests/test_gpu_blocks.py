@@ -147,3 +147,71 @@ def test_parallel_samples_attend_to_their_own_history(dev, n_samples):
     k2, v2 = oracle.pools_after_append(k1, v1, ref_slots, b.k_new, b.v_new)
     assert np.array_equal(_host(kc), k2) and np.array_equal(_host(vc), v2)
     assert np.array_equal(k2[prompt[:2]], k0[prompt[:2]])
+
+
+def test_prefix_cache_hit_equals_a_fresh_prefill(dev):
+    """[YB] 11.2.4 worked example on the device: request A (2,010 shared +
+    200 own tokens) is prefilled and registered, then finishes; request B
+    (the same 2,010 + 200 others) hits 125 blocks, appends and attends only
+    its last 210 rows.  B's output equals dense causal attention of those
+    rows over the KV of a fresh 2,210-token prefill (the shared positions'
+    KV is A's, since equal tokens give equal KV), and the pool holds A's
+    prefix untouched and B's tail bit for bit."""
+    nb, hkv, hq, D = 200, 8, 32, 128
+    rng = np.random.default_rng(31)
+    shared = rng.integers(0, 50000, size=2010).tolist()
+    tok_a = shared + rng.integers(0, 50000, size=200).tolist()
+    tok_b = shared + rng.integers(50000, 60000, size=200).tolist()
+    bits = lambda *shape: wl.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    scale = np.float32(1.0 / np.sqrt(D))
+    k0, v0 = _pools(nb, hkv, seed=32, normal=True)
+    kc, vc = _to_dev(k0, v0, dev)
+    pool = pkv.BlockPool(nb)
+
+    def run(tokens, q, k_new, v_new, row, k_pool, v_pool):
+        n_new = q.shape[0]
+        b = wl.Batch(name="prefix", num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                     cu_seqlens_q=np.array([0, n_new], np.int32), seq_lens=np.array([len(tokens)], np.int32),
+                     block_tables=row[None, :].copy(), num_blocks=nb, q=q, k_new=k_new, v_new=v_new,
+                     k_pool=k_pool, v_pool=v_pool, scale=scale)
+        t = {"q": pkv.bf16_tensor(q, dev), "k_new": pkv.bf16_tensor(k_new, dev),
+             "v_new": pkv.bf16_tensor(v_new, dev), "cu": torch.from_numpy(b.cu_seqlens_q).to(dev),
+             "sl": torch.from_numpy(b.seq_lens).to(dev), "bt": torch.from_numpy(b.block_tables).to(dev)}
+        plan = pkv.pkv_plan(b.cu_seqlens_q, b.seq_lens, hq, hkv, D, block_tables=b.block_tables,
+                            num_blocks=nb, device=dev)
+        out, slots = pkv.pkv_paged_step(t["q"], t["k_new"], t["v_new"], kc, vc, t["cu"], t["sl"], t["bt"],
+                                        float(scale), plan)
+        torch.cuda.synchronize()
+        return b, out, slots.cpu().numpy()
+
+    row_a = np.full(140, -1, np.int32)
+    assert pool.match_prefix(tok_a, row_a) == 0
+    assert pool.append_slots(row_a, 0, 2210) is None
+    q_a, k_a, v_a = bits(2210, hq, D), bits(2210, hkv, D), bits(2210, hkv, D)
+    note("prefix cache: request A prefill 2210 rows")
+    _, _, slots_a = run(tok_a, q_a, k_a, v_a, row_a, k0, v0)
+    k1, v1 = oracle.pools_after_append(k0, v0, slots_a, k_a, v_a)
+    pool.register_prefix(tok_a, row_a)
+    pool.release(row_a[:139][::-1])
+    assert pool.num_cached == 138
+
+    row_b = np.full(140, -1, np.int32)
+    cached = pool.match_prefix(tok_b, row_b)
+    assert cached == 2000 and np.array_equal(row_b[:125], row_a[:125])
+    assert pool.append_slots(row_b, cached, 2210 - cached) is None
+    q_b, k_b, v_b = bits(210, hq, D), bits(210, hkv, D), bits(210, hkv, D)
+    note("prefix cache: request B, 2000 cached + 210 rows")
+    b, out, slots_b = run(tok_b, q_b, k_b, v_b, row_b, k1, v1)
+    f64 = oracle.bf16_bits_to_f64
+    K = np.concatenate([f64(k_a[:2000]), f64(k_b)])
+    V = np.concatenate([f64(v_a[:2000]), f64(v_b)])
+    ref = oracle.attention_one_request(f64(q_b), K, V, 2000, float(scale))
+    got = f64(pkv.bf16_bits(out))
+    err = np.abs(got - ref)
+    note(f"prefix cache: max-abs {err.max():.3e} mean-abs {err.mean():.3e}")
+    assert np.isfinite(got).all() and err.max() <= 2e-2 and err.mean() <= 2e-3
+    assert np.array_equal(slots_b, oracle.slot_mapping(b.cu_seqlens_q, b.seq_lens, b.block_tables))
+    k2, v2 = oracle.pools_after_append(k1, v1, slots_b, k_b, v_b)
+    assert np.array_equal(_host(kc), k2) and np.array_equal(_host(vc), v2)
+    Kc, Vc = oracle.gather_kv(k2, v2, row_b, 2000, hkv, D)
+    assert np.array_equal(Kc, f64(k_a[:2000])) and np.array_equal(Vc, f64(v_a[:2000]))
