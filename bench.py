@@ -10,6 +10,10 @@ workload is the decode-only step: 64 sequences, one query row each,
 cached contexts uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128,
 bf16.
 
+Before every timed step a 1 GiB read evicts L2 and the Infinity Cache, so
+no step finds the previous one's KV on chip; step time and the attention
+launch are taken with HIP events on the library's stream, flush excluded.
+
 Prints ONE JSON line.  `value` is KV GB/s over the whole step (unique KV
 bytes / step time); query tok/s, the attention kernel's roofline fraction
 and the fp64 CPU oracle's rate on the same batch are reported beside it.
@@ -51,6 +55,8 @@ def parse():
     p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
     p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-flush", action="store_true",
+                   help="skip the 1 GiB read that evicts L2 and the Infinity Cache before each timed step")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time")
     p.add_argument("--narrow-waves", type=int, default=0, help="plan option (0 = library default)")
     p.add_argument("--min-wave-keys", type=int, default=0, help="plan option (0 = library default)")
@@ -95,6 +101,18 @@ def hbm_probe():
         ms = a.elapsed_time(b) / 10
         res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     print(json.dumps({"hbm_probe_GBs": res}), flush=True)
+
+
+def make_flush(dev, off: bool):
+    """A read of 1 GiB that leaves L2 and the 256 MB Infinity Cache holding
+    none of the step's data (a read, so the evicted lines are clean and no
+    write-back lands in the timed step); it runs before every step, outside
+    the step's events."""
+    import torch
+    if off:
+        return lambda: None
+    buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    return lambda: buf.sum()
 
 
 def kernel_source_sha256() -> str:
@@ -168,40 +186,46 @@ def main():
     out = torch.empty_like(t["q"])
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    new_ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(new_ev(), new_ev(), new_ev(), new_ev()) for _ in range(args.steps)]
+    flush = make_flush(dev, args.no_flush)
 
     def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
         pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"], t["block_tables"],
                             t["k_cache"], t["v_cache"], slot_mapping=slots, stream=stream)
         if i is not None:
-            ev[i][0].record(stream)
+            ev[i][1].record(stream)
         pkv.pkv_varlen_attention_main(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["scale"],
                                       plan, out=out, stream=stream)
         if i is not None:
-            ev[i][1].record(stream)
+            ev[i][2].record(stream)
         pkv.pkv_split_kv_reduce(plan, out, stream=stream)
+        if i is not None:
+            ev[i][3].record(stream)
 
     for _ in range(args.warmup):
+        flush()
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
-    t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_step = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     log(f"step {ms_step:.4f} ms, attention launch {attn_ms:.4f} ms")
 
     nbytes = accounting.step_bytes(batch.cu_seqlens_q, batch.seq_lens, batch.block_tables,
                                    batch.num_q_heads, batch.num_kv_heads, batch.head_dim)
     flop = accounting.attention_flop(batch.cu_seqlens_q, batch.seq_lens, batch.num_q_heads, batch.head_dim)
     kv_gbs = nbytes["kv_unique"] / (ms_step * 1e-3) / 1e9
-    attn_gbs = nbytes["total"] / (attn_ms * 1e-3) / 1e9
+    launch_bytes = nbytes["total"]
+    attn_gbs = launch_bytes / (attn_ms * 1e-3) / 1e9
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
-    hbm_bound = nbytes["total"] / (HBM_PEAK_GBS * 1e9) >= flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    hbm_bound = launch_bytes / (HBM_PEAK_GBS * 1e9) >= flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
@@ -210,7 +234,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     kernel = "attention_mixed_kernel" if plan.num_wide_items > 0 else "attention_kernel"
     roof.update({"traffic": measured_traffic(args.workload), "kernel": kernel, "avg_ms": round(attn_ms, 5),
-                 "bytes_per_launch": nbytes["total"], "flop_per_launch": flop})
+                 "bytes_per_launch": launch_bytes, "flop_per_launch": flop})
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -236,6 +260,7 @@ def main():
                    "waves": int(plan.num_waves) + int(plan.num_wide_items),
                    "wave_keys": int(plan.wave_keys)},
         "query_tok_s": round(batch.num_rows / (ms_step * 1e-3), 1),
+        "cache_flush_before_each_step": not args.no_flush,
         "kv_bytes_unique": nbytes["kv_unique"],
         "attention_flop": flop,
         "roofline": roof,

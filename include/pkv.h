@@ -161,7 +161,7 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * ------------------------------------------------------------------------- */
 typedef struct pkv_plan_options {
   int32_t narrow_waves;   /* wavefronts sharing the decode work (0 = default:
-                             1024; with wide tiles, 64 per row of narrow
+                             1536; with wide tiles, 64 per row of narrow
                              workgroups, rows sized to the estimated share of
                              the narrow work; at most 2048 with wide tiles) */
   int32_t min_wave_keys;  /* smallest share per wavefront, keys (0 = default) */

@@ -348,6 +348,11 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) ch.v[dt] &= keep;
     }
+    // Only a chunk that reaches past k1 or past the tile's first position
+    // can hold keys some column must not see; inside the others every key
+    // is visible to every column.  Columns past the tile (no query) see
+    // whatever they see: their results are never written.
+    const bool edge = key0 + 32 > it.k1 || key0 + 31 > it.pos0;
     u32x4 pb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -360,33 +365,41 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
       float sv[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[i] = s0[i] * a.scale_log2;
-        sv[4 + i] = s1[i] * a.scale_log2;
+        sv[i] = s0[i];
+        sv[4 + i] = s1[i];
+      }
+      if (edge) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = kl + j;
+          sv[j] = key < it.k1 && key <= col_pos[nt] ? sv[j] : neg_inf();
+        }
       }
       float mx = neg_inf();
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = kl + j;
-        const bool ok = col_ok[nt] && key < it.k1 && key <= col_pos[nt];
-        sv[j] = ok ? sv[j] : neg_inf();
-        mx = fmaxf(mx, sv[j]);
-      }
-      mx = xmax32(xmax16(mx));
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+      // raw scores until here: the scale (> 0) commutes with the maximum
+      mx = xmax32(xmax16(mx)) * a.scale_log2;
       const float m_new = fmaxf(m_run[nt], mx);
       const float m_use = m_new == neg_inf() ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       float lsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(sv[2 * i] - m_use),
-                                     __builtin_amdgcn_exp2f(sv[2 * i + 1] - m_use));
+        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], a.scale_log2, -m_use)),
+                                     __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], a.scale_log2, -m_use)));
         pb[nt][i] = w;
         lsum += bf16_lo(w) + bf16_hi(w);
       }
-      l_run[nt] = l_run[nt] * alpha + lsum;
-      m_run[nt] = m_new;
+      // rescale only when some column's maximum moved (wave-uniform test)
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run[nt])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+        l_run[nt] = l_run[nt] * alpha + lsum;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) acc[nt][dt] *= alpha;
+      } else {
+        l_run[nt] += lsum;
+      }
+      m_run[nt] = m_new;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)

@@ -33,7 +33,9 @@ namespace {
 using pkv::Item;
 using pkv::Merge;
 
-constexpr int kDefaultNarrowWaves = 1024;  // one per SIMD on 256 CUs
+// six per CU of 256: measured on MI355X decode steps, 3-4% faster than one
+// per SIMD (1024) or two per SIMD (2048)
+constexpr int kDefaultNarrowWaves = 1536;
 constexpr int kDefaultMinWaveKeys = 512;
 constexpr int kDefaultWorkgroups = 256;    // one per CU on an MI355X
 constexpr int kXcds = 8;                   // consecutive workgroups go to the XCDs in turn

@@ -184,7 +184,7 @@ def test_plan_accounting_matches_visibility_counts():
 def test_plan_splits_long_decode_contexts():
     b = wl.config_long_shared()
     plan = _plan(b.cu_seqlens_q, b.seq_lens)
-    assert plan.num_waves == 1024 and plan.num_merge == 16 * 32
+    assert plan.num_waves == 1536 and plan.num_merge == 16 * 32
     _coverage(plan, b.cu_seqlens_q, b.seq_lens, 32, 8)
     _check_waves(plan)
 
