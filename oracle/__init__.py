@@ -29,3 +29,5 @@ from .paged_attention import (  # noqa: F401
     score_shapes,
     step_from_batch,
 )
+
+from . import layer  # noqa: F401,E402
