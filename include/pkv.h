@@ -262,6 +262,63 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
                    pkv_stream_t stream);
 
 /* ===========================================================================
+ * The weight layers around the step: one packed layer.
+ * ======================================================================== */
+
+/* ---------------------------------------------------------------------------
+ * Linear layer over all packed rows ("11.2 连续批处理与 PagedAttention",
+ * section 11.2.2: the weight layers take the step's rows of every request
+ * as one matrix, X[7, 4096] x W_Q[4096, 4096] -> Q[7, 4096] in the worked
+ * example; "continuous batching" (k4i.top), section "把 prefill 和 decode
+ * 打包在一起": Q = X W_Q over the packed rows).
+ *   y[m][n] = sum_k x[m][k] * w[n][k]
+ * x: device bf16[M][K] row-major; w: device bf16[N][K] (weights stored
+ * [out features][in features], the transpose of the pages' W_Q); y: device
+ * bf16[M][N].  fp32 accumulation, bf16 result (nearest even).  N must be a
+ * multiple of 128 and K a positive multiple of 64 (PKV_EUNSUPPORTED
+ * otherwise); M is any size.  Errors: PKV_EINVAL (null pointer, negative
+ * size), PKV_ERANGE (grid too large), PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_linear(const pkv_bf16 *x, const pkv_bf16 *w, int32_t M, int32_t N, int32_t K, pkv_bf16 *y,
+               pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fused QKV projection with RoPE (same passages; k4i.top: RoPE sees each
+ * request's own position id).  w_qkv: device bf16[(Hq + 2 Hkv) * 128][hidden],
+ * the query heads' 128 rows each, then the key heads', then the value
+ * heads'.  For packed row t of sequence s at position
+ * p = seq_lens[s] - q_len_s + (t - cu_seqlens_q[s]) (device int32 arrays of
+ * num_seqs + 1 and num_seqs entries), the projection x[t] w_qkv^T is split
+ * into heads; every query and key head is rotated: for i < 64 the pair
+ * (d_i, d_{i+64}) turns by the angle p * rope_theta^(-2i/128) (RoFormer's
+ * rotation with the two halves of a head as the pair's parts; the pages do
+ * not give the formula), values are not.  Outputs: q bf16[T][Hq][128],
+ * k_new and v_new bf16[T][Hkv][128] -- the step's inputs.  hidden must be a
+ * multiple of 64; rope_theta > 1 (PKV_EINVAL otherwise).
+ * ------------------------------------------------------------------------- */
+int pkv_qkv_rope(const pkv_bf16 *x, const pkv_bf16 *w_qkv, int32_t num_rows, int32_t hidden,
+                 const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                 int32_t num_kv_heads, float rope_theta, pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new,
+                 pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One packed attention layer on one stream ("11.2 连续批处理与
+ * PagedAttention", section 11.2.2: weight layers over all rows, the new K
+ * and V appended to each request's cache, attention per request, results
+ * back as one [T, 4096] matrix): pkv_qkv_rope, pkv_paged_step, then
+ * y = attn w_o^T with pkv_linear.  w_o: device bf16[hidden][Hq * 128].
+ * The caller provides q, k_new, v_new (as above) and attn bf16[T][Hq][128];
+ * y: bf16[T][hidden].  The plan, workspace, pools and metadata are those of
+ * pkv_paged_step.  Errors: those of the three calls.
+ * ------------------------------------------------------------------------- */
+int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *w_o, int32_t hidden,
+                      pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                      const int32_t *block_tables, int32_t bt_stride, int64_t num_blocks, int64_t *slot_mapping,
+                      float scale, float rope_theta, const pkv_plan_t *plan, void *ws, size_t ws_bytes,
+                      pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new, pkv_bf16 *attn, pkv_bf16 *y,
+                      pkv_stream_t stream);
+
+/* ===========================================================================
  * Block pool, copy-on-write and swap (the steps either side of the append).
  * ======================================================================== */
 

@@ -16,6 +16,10 @@ from .binding import (  # noqa: F401
     load_library,
     pkv_block_hash,
     pkv_copy_blocks,
+    pkv_layer_forward,
+    pkv_linear,
+    pkv_qkv_rope,
+    ROPE_THETA,
     pkv_paged_kv_append,
     pkv_paged_step,
     pkv_paged_varlen_attention,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpkv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["pkv_kernels.hip", "pkv_plan.cpp", "pkv_blocks.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_layer.hip", "pkv_plan.cpp", "pkv_blocks.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

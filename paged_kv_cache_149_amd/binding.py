@@ -80,6 +80,10 @@ _SIGNATURES = {
                                                   ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
     "pkv_paged_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
                                       ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_linear": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "pkv_qkv_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _P, _P, _P]),
+    "pkv_layer_forward": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I64, _P, _F, _F,
+                                         ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "pkv_block_pool_create": (ctypes.c_int, [_I64, ctypes.POINTER(ctypes.c_void_p)]),
     "pkv_block_pool_destroy": (None, [_P]),
     "pkv_block_pool_num_free": (_I64, [_P]),
@@ -372,6 +376,92 @@ def pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, bl
         _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], nb, _ptr(slot_mapping),
         float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
     return out, slot_mapping
+
+
+# ---------------------------------------------------------------------------
+# the weight layers around the step
+# ---------------------------------------------------------------------------
+
+ROPE_THETA = 500000.0
+
+
+def pkv_linear(x, w, out=None, stream=None):
+    """y = x w^T over all rows: x bf16 [M, K], w bf16 [N, K] -> y bf16 [M, N]."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev)
+    _need(w, "w", torch.bfloat16, dev)
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] with x's K")
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check("pkv_linear", lib.pkv_linear(_ptr(x), _ptr(w), M, N, K, _ptr(out), _stream(stream, dev)))
+    return out
+
+
+def _qkv_out(T, Hq, Hkv, dev):
+    return (torch.empty(T, Hq, HEAD_DIM, dtype=torch.bfloat16, device=dev),
+            torch.empty(T, Hkv, HEAD_DIM, dtype=torch.bfloat16, device=dev),
+            torch.empty(T, Hkv, HEAD_DIM, dtype=torch.bfloat16, device=dev))
+
+
+def pkv_qkv_rope(x, w_qkv, cu_seqlens_q, seq_lens, num_q_heads: int, num_kv_heads: int,
+                 rope_theta: float = ROPE_THETA, stream=None):
+    """The fused QKV projection with RoPE by each row's position; returns
+    (q [T, Hq, 128], k_new [T, Hkv, 128], v_new [T, Hkv, 128])."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev)
+    _need(w_qkv, "w_qkv", torch.bfloat16, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    T, hidden = x.shape
+    if tuple(w_qkv.shape) != ((num_q_heads + 2 * num_kv_heads) * HEAD_DIM, hidden):
+        raise ValueError("w_qkv must be [(Hq + 2 Hkv) * 128, hidden]")
+    q, k, v = _qkv_out(T, num_q_heads, num_kv_heads, dev)
+    _check("pkv_qkv_rope", lib.pkv_qkv_rope(
+        _ptr(x), _ptr(w_qkv), T, hidden, _ptr(cu_seqlens_q), _ptr(seq_lens), seq_lens.numel(), num_q_heads,
+        num_kv_heads, float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _stream(stream, dev)))
+    return q, k, v
+
+
+def pkv_layer_forward(x, w_qkv, w_o, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, scale, plan: Plan,
+                      rope_theta: float = ROPE_THETA, buffers=None, stream=None):
+    """One packed layer: QKV projection with RoPE, the paged step, output
+    projection.  Returns (y [T, hidden], buffers) where buffers holds the
+    q, k_new, v_new, attn and slot_mapping tensors it wrote (pass them back
+    in to reuse them)."""
+    lib = load_library()
+    dev = x.device
+    T, hidden = x.shape
+    Hq, Hkv = plan.st.num_q_heads, plan.st.num_kv_heads
+    for t, name in ((x, "x"), (w_qkv, "w_qkv"), (w_o, "w_o"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, torch.bfloat16, dev)
+    for t, name in ((cu_seqlens_q, "cu_seqlens_q"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        _need(t, name, torch.int32, dev)
+    if T != plan.st.num_rows:
+        raise ValueError("x does not match the plan")
+    if tuple(w_o.shape) != (hidden, Hq * HEAD_DIM):
+        raise ValueError("w_o must be [hidden, Hq * 128]")
+    if buffers is None:
+        q, k, v = _qkv_out(T, Hq, Hkv, dev)
+        buffers = {"q": q, "k_new": k, "v_new": v, "attn": torch.empty_like(q),
+                   "slot_mapping": torch.empty(T, dtype=torch.int64, device=dev),
+                   "y": torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)}
+    nb = k_cache.shape[0]
+    ws = plan.workspace
+    bf = buffers
+    _check("pkv_layer_forward", lib.pkv_layer_forward(
+        _ptr(x), _ptr(w_qkv), _ptr(w_o), hidden, _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), _ptr(seq_lens),
+        _ptr(block_tables), block_tables.shape[1], nb, _ptr(bf["slot_mapping"]), float(scale), float(rope_theta),
+        ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(bf["q"]), _ptr(bf["k_new"]), _ptr(bf["v_new"]),
+        _ptr(bf["attn"]), _ptr(bf["y"]), _stream(stream, dev)))
+    return bf["y"], bf
 
 
 # ---------------------------------------------------------------------------

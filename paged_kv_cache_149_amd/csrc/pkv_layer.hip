@@ -1,0 +1,325 @@
+// The weight layers of one packed layer around the paged step, written for
+// CDNA4 (gfx950, wave64, bf16 MFMA): the projections run over all packed
+// rows at once, attention per request ("11.2 连续批处理与 PagedAttention",
+// section 11.2.2, selective batching: X[7, 4096] x W_Q -> Q[7, 4096]; and
+// "continuous batching" (k4i.top), section "把 prefill 和 decode 打包在一起":
+// Q = X W_Q, K = X W_K, V = X W_V over the packed rows, RoPE by each row's
+// own position id).
+//
+//   linear_kernel<false>  y[m][n] = sum_k x[m][k] w[n][k]   (bf16 in, fp32
+//                         accumulate, bf16 out, nearest even)
+//   linear_kernel<true>   the fused QKV projection: the same product with
+//                         w = [query heads; key heads; value heads] x 128
+//                         rows, RoPE applied to query and key heads by each
+//                         row's position, written as q [T][Hq][128],
+//                         k_new and v_new [T][Hkv][128]
+//
+// Weights are [out features][in features], so an output feature's weights
+// and an input row are both contiguous over the inner dimension and every
+// MFMA operand is one 16-byte piece of a row.  A workgroup computes a tile
+// of 256 rows x 128 features (one head) in 64-deep stages staged through
+// LDS (double buffered, the next stage's global loads in flight while the
+// current one is multiplied); wavefront w owns rows 64w .. 64w + 63 and all
+// 128 features, as D^T = W X^T with v_mfma_f32_16x16x32_bf16:
+//   A operand (features): lane l holds W[16j + l%16][8(l/16) .. +7]
+//   B operand (rows):     lane l holds X[16i + l%16][8(l/16) .. +7]
+//   D[feature][row]:      lane l holds features 16j + 4(l/16) .. +3 of row
+//                         16i + l%16 -- four consecutive outputs of one row
+// so feature d and its RoPE partner d + 64 (tiles j and j + 4) sit in the
+// same lane, and the rotation needs no data exchange.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pkv_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 256;              // rows per tile
+constexpr int kBN = 128;              // features per tile (one head of 128)
+constexpr int kBK = 64;               // inner dimension per stage
+constexpr int kRow = kBK + 8;         // LDS row pitch, bf16: 144 bytes, so the 16 rows of a
+                                      // fragment read start in 16 different bank quads
+constexpr int kStage = (kBM + kBN) * kRow;  // bf16 per stage buffer
+constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+__device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// two floats to bf16 (nearest even), lo in the low half
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+struct LinearArgs {
+  const uint16_t *x;  // [M][K]
+  const uint16_t *w;  // [N][K]
+  uint16_t *y;        // [M][N] (plain product)
+  int32_t M, N, K;
+  int32_t tiles_m;        // row tiles
+  int32_t tiles_per_xcd;  // tiles dealt to each XCD (grid = 8 x this)
+  // fused QKV projection
+  uint16_t *q, *k, *v;
+  const int32_t *cu, *seq_lens;
+  int32_t S, Hq, Hkv;
+  double rope_log2_step;  // log2(theta) * 2 / 128: pair i turns by p * 2^(-i * step) radians
+};
+
+// position of packed row t: its sequence s (last s with cu[s] <= t), then
+// seq_lens[s] - q_len_s + (t - cu[s])
+__device__ inline int row_position(const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens, int S,
+                                   int t) {
+  int lo = 0, hi = S;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo < S ? lo : S - 1;
+  return seq_lens[s] - (cu[s + 1] - cu[s]) + (t - cu[s]);
+}
+
+// Turns per position of pair i: theta^(-2i/128) / (2 pi) = 2^(-i * step) /
+// (2 pi), in double: at position p ~ 3e4 the angle is ~5e3 turns, and a
+// float's 2^-24 relative error there would already move it by ~2e-3 rad.
+__device__ inline double rope_turns_per_pos(int i, double step) {
+  return exp2(-(double)i * step) * 0.15915494309189533577;
+}
+
+// cos and sin of p * f turns: the product in double, reduced to [-1/2, 1/2]
+// turns, then taken back to radians in float.
+__device__ inline void rope_cos_sin(double p, double f, float &c, float &s) {
+  const double turns = p * f;
+  const float a = (float)(turns - rint(turns)) * 6.283185307179586f;
+  c = __cosf(a);
+  s = __sinf(a);
+}
+
+template <bool kRope>
+__global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  // blocks go to the XCDs in turn: XCD x takes tiles x * tiles_per_xcd ..,
+  // rows fastest, so the blocks resident on one XCD share their weight tile
+  const int b = blockIdx.x;
+  const int t = (b % kXcds) * g.tiles_per_xcd + b / kXcds;
+  if (t >= g.tiles_m * (g.N / kBN)) return;
+  const int n_tile = t / g.tiles_m, m_tile = t % g.tiles_m;
+  const int m0 = m_tile * kBM, n0 = n_tile * kBN;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
+
+  // Stage loads: thread tid moves 16-byte pieces c = tid + 256u, row c / 8,
+  // column piece c % 8 -- eight of the row tile (rows past M read as zero)
+  // and four of the weight tile.
+  u32x4 px[8], pw[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      px[u] = m0 + row < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)(m0 + row) * g.K + k0 + 8 * col)
+                             : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      pw[u] = *reinterpret_cast<const u32x4 *>(g.w + (int64_t)(n0 + row) * g.K + k0 + 8 * col);
+    }
+  };
+  auto stash = [&](int buf) {
+    uint16_t *xs = lds + buf * kStage, *ws = xs + kBM * kRow;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      *reinterpret_cast<u32x4 *>(xs + row * kRow + 8 * col) = px[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      *reinterpret_cast<u32x4 *>(ws + row * kRow + 8 * col) = pw[u];
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = g.K / kBK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nk) fetch((s + 1) * kBK);
+    const uint16_t *xs = lds + buf * kStage, *ws = xs + kBM * kRow;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4 wf[8], xf[4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        wf[j] = *reinterpret_cast<const u32x4 *>(ws + (16 * j + r) * kRow + 32 * sub + 8 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        xf[i] = *reinterpret_cast<const u32x4 *>(xs + (64 * wv + 16 * i + r) * kRow + 32 * sub + 8 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma(wf[j], xf[i], acc[i][j]);
+    }
+    // the other buffer was last read before the previous barrier
+    if (s + 1 < nk) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!kRope) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 64 * wv + 16 * i + r;
+      if (m >= g.M) continue;
+      uint16_t *yr = g.y + (int64_t)m * g.N + n0 + 4 * gq;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<u32x2 *>(yr + 16 * j) =
+            u32x2{pack_bf16(acc[i][j][0], acc[i][j][1]), pack_bf16(acc[i][j][2], acc[i][j][3])};
+    }
+    return;
+  }
+
+  // fused QKV: tile n_tile is query head n_tile, key head n_tile - Hq or
+  // value head n_tile - Hq - Hkv
+  uint16_t *dst;
+  int H, hh;
+  if (n_tile < g.Hq) {
+    dst = g.q; H = g.Hq; hh = n_tile;
+  } else if (n_tile < g.Hq + g.Hkv) {
+    dst = g.k; H = g.Hkv; hh = n_tile - g.Hq;
+  } else {
+    dst = g.v; H = g.Hkv; hh = n_tile - g.Hq - g.Hkv;
+  }
+  const bool rotate = n_tile < g.Hq + g.Hkv;
+  // this lane's pairs are i = 16j + 4(l/16) + e, j, e < 4
+  double f[4][4];
+  if (rotate) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[j][e] = rope_turns_per_pos(16 * j + 4 * gq + e, g.rope_log2_step);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wv + 16 * i + r;
+    if (m >= g.M) continue;
+    f32x4 o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = acc[i][j];
+    if (rotate) {
+      const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float c, s;
+          rope_cos_sin(p, f[j][e], c, s);
+          const float x1 = acc[i][j][e], x2 = acc[i][j + 4][e];
+          o[j][e] = x1 * c - x2 * s;
+          o[j + 4][e] = x2 * c + x1 * s;
+        }
+    }
+    uint16_t *dr = dst + ((int64_t)m * H + hh) * kBN + 4 * gq;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x2 *>(dr + 16 * j) = u32x2{pack_bf16(o[j][0], o[j][1]), pack_bf16(o[j][2], o[j][3])};
+  }
+}
+
+inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s); }
+
+int launch_linear(LinearArgs g, bool rope, pkv_stream_t stream) {
+  g.tiles_m = (g.M + kBM - 1) / kBM;
+  const int64_t tiles = (int64_t)g.tiles_m * (g.N / kBN);
+  if (tiles == 0) return PKV_OK;
+  g.tiles_per_xcd = (int32_t)((tiles + kXcds - 1) / kXcds);
+  if ((int64_t)g.tiles_per_xcd * kXcds > INT32_MAX) return PKV_ERANGE;
+  const dim3 grid((unsigned)(g.tiles_per_xcd * kXcds));
+  if (rope)
+    hipLaunchKernelGGL(linear_kernel<true>, grid, dim3(kThreads), 0, as_stream(stream), g);
+  else
+    hipLaunchKernelGGL(linear_kernel<false>, grid, dim3(kThreads), 0, as_stream(stream), g);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_linear(const pkv_bf16 *x, const pkv_bf16 *w, int32_t M, int32_t N, int32_t K, pkv_bf16 *y,
+               pkv_stream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return PKV_EINVAL;
+  if (N % kBN != 0 || K % kBK != 0) return PKV_EUNSUPPORTED;
+  if (M == 0 || N == 0) return PKV_OK;
+  if (K == 0) return PKV_EUNSUPPORTED;
+  if (!x || !w || !y) return PKV_EINVAL;
+  LinearArgs g{};
+  g.x = x;
+  g.w = w;
+  g.y = y;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launch_linear(g, false, stream);
+}
+
+int pkv_qkv_rope(const pkv_bf16 *x, const pkv_bf16 *w_qkv, int32_t num_rows, int32_t hidden,
+                 const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                 int32_t num_kv_heads, float rope_theta, pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new,
+                 pkv_stream_t stream) {
+  if (num_rows < 0 || hidden <= 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  if (hidden % kBK != 0) return PKV_EUNSUPPORTED;
+  if (!(rope_theta > 1.f) || !std::isfinite(rope_theta)) return PKV_EINVAL;
+  if (num_rows == 0) return PKV_OK;
+  if (!x || !w_qkv || !cu_seqlens_q || !seq_lens || !q || !k_new || !v_new || num_seqs == 0) return PKV_EINVAL;
+  LinearArgs g{};
+  g.x = x;
+  g.w = w_qkv;
+  g.M = num_rows;
+  g.N = (num_q_heads + 2 * num_kv_heads) * pkv::kHeadDim;
+  g.K = hidden;
+  g.q = q;
+  g.k = k_new;
+  g.v = v_new;
+  g.cu = cu_seqlens_q;
+  g.seq_lens = seq_lens;
+  g.S = num_seqs;
+  g.Hq = num_q_heads;
+  g.Hkv = num_kv_heads;
+  g.rope_log2_step = std::log2((double)rope_theta) * 2.0 / pkv::kHeadDim;
+  return launch_linear(g, true, stream);
+}
+
+int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *w_o, int32_t hidden,
+                      pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                      const int32_t *block_tables, int32_t bt_stride, int64_t num_blocks, int64_t *slot_mapping,
+                      float scale, float rope_theta, const pkv_plan_t *plan, void *ws, size_t ws_bytes,
+                      pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new, pkv_bf16 *attn, pkv_bf16 *y,
+                      pkv_stream_t stream) {
+  if (!plan) return PKV_EINVAL;
+  int st = pkv_qkv_rope(x, w_qkv, plan->num_rows, hidden, cu_seqlens_q, seq_lens, plan->num_seqs,
+                        plan->num_q_heads, plan->num_kv_heads, rope_theta, q, k_new, v_new, stream);
+  if (st != PKV_OK) return st;
+  st = pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, bt_stride,
+                      num_blocks, slot_mapping, scale, plan, ws, ws_bytes, attn, stream);
+  if (st != PKV_OK) return st;
+  return pkv_linear(attn, w_o, plan->num_rows, hidden, plan->num_q_heads * pkv::kHeadDim, y, stream);
+}
+
+}  // extern "C"
