@@ -51,8 +51,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap", "prefixcache"])
+    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap", "prefixcache", "layer"])
     p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
+    p.add_argument("--layer-batch", default="mixed", choices=sorted(WORKLOADS),
+                   help="layer workload: the step whose rows the layer runs on")
     p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true",
@@ -170,6 +172,9 @@ def main():
         return
     if args.workload == "prefixcache":
         run_prefix(args)
+        return
+    if args.workload == "layer":
+        run_layer(args)
         return
     dev = torch.device("cuda", 0)
     pkv.load_library()
@@ -555,6 +560,99 @@ def run_prefix(args):
                         "kernel": "attention (warm step)", "avg_ms": round(warm_attn, 5),
                         "flop_per_launch": warm_flop, "cold_avg_ms": round(cold_attn, 5),
                         "cold_TFLOPs": round(cold_flop / (cold_attn * 1e-3) / 1e12, 2)}}
+    print(json.dumps(res), flush=True)
+
+
+def run_layer(args):
+    """One packed attention layer (hidden 4096, 32 query / 8 KV heads of
+    128) on the rows of a step workload: the fused QKV projection with RoPE,
+    the paged step (append, attention, merge) and the output projection,
+    each launch bracketed by HIP events; L2 and the Infinity Cache evicted
+    before every step.  Weights are random N(0, 1/fan_in) bf16."""
+    import torch
+    import paged_kv_cache_149_amd as pkv
+    from paged_kv_cache_149_amd import accounting
+    from synth import workloads as wl
+    from synth.device import to_device
+    dev = torch.device("cuda", 0)
+    pkv.load_library()
+    batch = getattr(wl, WORKLOADS[args.layer_batch])()
+    T, Hq, Hkv, D, hidden = batch.num_rows, batch.num_q_heads, batch.num_kv_heads, batch.head_dim, 4096
+    log(f"layer on {batch.name}: {T} rows, hidden {hidden}")
+    t = to_device(batch, dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev).manual_seed(149300)
+    x = torch.randn(T, hidden, device=dev, generator=g).to(torch.bfloat16)
+    w_qkv = (torch.randn((Hq + 2 * Hkv) * D, hidden, device=dev, generator=g) / hidden ** 0.5).to(torch.bfloat16)
+    w_o = (torch.randn(hidden, Hq * D, device=dev, generator=g) / (Hq * D) ** 0.5).to(torch.bfloat16)
+    plan = pkv.pkv_plan(batch.cu_seqlens_q, batch.seq_lens, Hq, Hkv, D, block_tables=batch.block_tables,
+                        num_blocks=batch.num_blocks, device=dev, stream=stream)
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+    attn = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(T, hidden, dtype=torch.bfloat16, device=dev)
+    flush = make_flush(dev, args.no_flush)
+    new_ev = lambda: torch.cuda.Event(enable_timing=True)
+    names = ["qkv_rope", "append", "attention", "merge", "o_proj"]
+    ev = [[new_ev() for _ in range(len(names) + 1)] for _ in range(args.steps)]
+
+    def step(i=None):
+        mark = (lambda k: ev[i][k].record(stream)) if i is not None else (lambda k: None)
+        mark(0)
+        q, k_new, v_new = pkv.pkv_qkv_rope(x, w_qkv, t["cu_seqlens_q"], t["seq_lens"], Hq, Hkv, stream=stream)
+        mark(1)
+        pkv.pkv_slot_append(k_new, v_new, t["cu_seqlens_q"], t["seq_lens"], t["block_tables"], t["k_cache"],
+                            t["v_cache"], slot_mapping=slots, stream=stream)
+        mark(2)
+        pkv.pkv_varlen_attention_main(q, t["k_cache"], t["v_cache"], t["block_tables"], t["scale"], plan,
+                                      out=attn, stream=stream)
+        mark(3)
+        pkv.pkv_split_kv_reduce(plan, attn, stream=stream)
+        mark(4)
+        pkv.pkv_linear(attn.view(T, Hq * D), w_o, out=y, stream=stream)
+        mark(5)
+
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        flush()
+        step(i)
+    torch.cuda.synchronize()
+    ms = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in ev])) for k, n in enumerate(names)}
+    layer_ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in ev]))
+    qkv_flop = 2.0 * T * hidden * (Hq + 2 * Hkv) * D
+    o_flop = 2.0 * T * Hq * D * hidden
+    nbytes = accounting.step_bytes(batch.cu_seqlens_q, batch.seq_lens, batch.block_tables, Hq, Hkv, D)
+    flop = accounting.attention_flop(batch.cu_seqlens_q, batch.seq_lens, Hq, D)
+    kern = {
+        "qkv_rope": {"TFLOP/s": qkv_flop / (ms["qkv_rope"] * 1e-3) / 1e12, "flop": qkv_flop},
+        "attention": {"GB/s": nbytes["total"] / (ms["attention"] * 1e-3) / 1e9,
+                      "TFLOP/s": flop / (ms["attention"] * 1e-3) / 1e12},
+        "o_proj": {"TFLOP/s": o_flop / (ms["o_proj"] * 1e-3) / 1e12, "flop": o_flop},
+    }
+    dominant = max(("qkv_rope", "attention", "o_proj"), key=lambda n: ms[n])
+    if dominant == "attention":
+        hbm = nbytes["total"] / (HBM_PEAK_GBS * 1e9) >= flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+        a = kern["attention"]["GB/s" if hbm else "TFLOP/s"]
+        peak = HBM_PEAK_GBS if hbm else BF16_MFMA_PEAK_TFLOPS
+        roof = {"bound": "hbm" if hbm else "mfma", "achieved": round(a, 1), "peak": peak,
+                "unit": "GB/s" if hbm else "TFLOP/s", "frac": round(a / peak, 4), "kernel": "attention"}
+    else:
+        a = kern[dominant]["TFLOP/s"]
+        roof = {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / BF16_MFMA_PEAK_TFLOPS, 4), "kernel": f"linear_kernel ({dominant})"}
+    roof.update({"traffic": None, "avg_ms": round(ms[dominant], 5)})
+    res = {"metric": "packed attention layer (QKV+RoPE, paged step, O projection): rows/s, 1 GPU",
+           "value": round(T / (layer_ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(layer_ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"layer-h{hidden}-{batch.name}", "rows": T, "hidden": hidden, "q_heads": Hq,
+                      "kv_heads": Hkv, "head_dim": D},
+           "ms_per_launch": {n: round(v, 5) for n, v in ms.items()},
+           "kernels": {n: {k: round(v, 2) if isinstance(v, float) and k != "flop" else v for k, v in d.items()}
+                       for n, d in kern.items()},
+           "cache_flush_before_each_step": not args.no_flush, "roofline": roof}
     print(json.dumps(res), flush=True)
 
 

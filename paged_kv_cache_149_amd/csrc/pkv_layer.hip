@@ -16,11 +16,13 @@
 //
 // Weights are [out features][in features], so an output feature's weights
 // and an input row are both contiguous over the inner dimension and every
-// MFMA operand is one 16-byte piece of a row.  A workgroup computes a tile
-// of 256 rows x 128 features (one head) in 64-deep stages staged through
-// LDS (double buffered, the next stage's global loads in flight while the
-// current one is multiplied); wavefront w owns rows 64w .. 64w + 63 and all
-// 128 features, as D^T = W X^T with v_mfma_f32_16x16x32_bf16:
+// MFMA operand is one 16-byte piece of a row.  A workgroup of eight
+// wavefronts (two per SIMD, so one's matrix work hides the other's LDS
+// reads) computes a tile of 256 rows x 256 features (two heads) in 64-deep
+// stages staged through LDS (double buffered, the next stage's global loads
+// in flight while the current one is multiplied); wavefront w owns rows
+// 64 (w % 4) .. +63 and the 128 features of head w / 4, as D^T = W X^T with
+// v_mfma_f32_16x16x32_bf16:
 //   A operand (features): lane l holds W[16j + l%16][8(l/16) .. +7]
 //   B operand (rows):     lane l holds X[16i + l%16][8(l/16) .. +7]
 //   D[feature][row]:      lane l holds features 16j + 4(l/16) .. +3 of row
@@ -44,12 +46,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 256;              // rows per tile
-constexpr int kBN = 128;              // features per tile (one head of 128)
+constexpr int kBN = 256;              // features per tile (two heads of 128)
+constexpr int kHead = 128;            // features per wavefront (one head)
 constexpr int kBK = 64;               // inner dimension per stage
 constexpr int kRow = kBK + 8;         // LDS row pitch, bf16: 144 bytes, so the 16 rows of a
                                       // fragment read start in 16 different bank quads
 constexpr int kStage = (kBM + kBN) * kRow;  // bf16 per stage buffer
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -112,38 +115,33 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   // rows fastest, so the blocks resident on one XCD share their weight tile
   const int b = blockIdx.x;
   const int t = (b % kXcds) * g.tiles_per_xcd + b / kXcds;
-  if (t >= g.tiles_m * (g.N / kBN)) return;
+  if (t >= g.tiles_m * ((g.N + kBN - 1) / kBN)) return;
   const int n_tile = t / g.tiles_m, m_tile = t % g.tiles_m;
   const int m0 = m_tile * kBM, n0 = n_tile * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
+  // wavefront wv: rows 64 (wv % 4) .., features (head) 128 (wv / 4) ..
+  const int wm = wv & 3, wn = wv >> 2;
 
-  // Stage loads: thread tid moves 16-byte pieces c = tid + 256u, row c / 8,
-  // column piece c % 8 -- eight of the row tile (rows past M read as zero)
-  // and four of the weight tile.
-  u32x4 px[8], pw[4];
+  // Stage loads: thread tid moves 16-byte pieces c = tid + 512u, row c / 8,
+  // column piece c % 8 -- four of the row tile (rows past M read as zero)
+  // and four of the weight tile (rows past N read as zero).
+  u32x4 px[4], pw[4];
   auto fetch = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
-      px[u] = m0 + row < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)(m0 + row) * g.K + k0 + 8 * col)
-                             : u32x4{0, 0, 0, 0};
-    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
-      pw[u] = *reinterpret_cast<const u32x4 *>(g.w + (int64_t)(n0 + row) * g.K + k0 + 8 * col);
+      px[u] = m0 + row < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)(m0 + row) * g.K + k0 + 8 * col)
+                             : u32x4{0, 0, 0, 0};
+      pw[u] = n0 + row < g.N ? *reinterpret_cast<const u32x4 *>(g.w + (int64_t)(n0 + row) * g.K + k0 + 8 * col)
+                             : u32x4{0, 0, 0, 0};
     }
   };
   auto stash = [&](int buf) {
     uint16_t *xs = lds + buf * kStage, *ws = xs + kBM * kRow;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
-      *reinterpret_cast<u32x4 *>(xs + row * kRow + 8 * col) = px[u];
-    }
-#pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      *reinterpret_cast<u32x4 *>(xs + row * kRow + 8 * col) = px[u];
       *reinterpret_cast<u32x4 *>(ws + row * kRow + 8 * col) = pw[u];
     }
   };
@@ -167,10 +165,10 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
       u32x4 wf[8], xf[4];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        wf[j] = *reinterpret_cast<const u32x4 *>(ws + (16 * j + r) * kRow + 32 * sub + 8 * gq);
+        wf[j] = *reinterpret_cast<const u32x4 *>(ws + (kHead * wn + 16 * j + r) * kRow + 32 * sub + 8 * gq);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xf[i] = *reinterpret_cast<const u32x4 *>(xs + (64 * wv + 16 * i + r) * kRow + 32 * sub + 8 * gq);
+        xf[i] = *reinterpret_cast<const u32x4 *>(xs + (64 * wm + 16 * i + r) * kRow + 32 * sub + 8 * gq);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -181,12 +179,14 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
     __syncthreads();
   }
 
+  const int nw = n0 + kHead * wn;  // this wavefront's first feature
+  if (nw >= g.N) return;           // past N (N an odd multiple of 128)
   if (!kRope) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 64 * wv + 16 * i + r;
+      const int m = m0 + 64 * wm + 16 * i + r;
       if (m >= g.M) continue;
-      uint16_t *yr = g.y + (int64_t)m * g.N + n0 + 4 * gq;
+      uint16_t *yr = g.y + (int64_t)m * g.N + nw + 4 * gq;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         *reinterpret_cast<u32x2 *>(yr + 16 * j) =
@@ -195,18 +195,19 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
     return;
   }
 
-  // fused QKV: tile n_tile is query head n_tile, key head n_tile - Hq or
-  // value head n_tile - Hq - Hkv
+  // fused QKV: this wavefront's head of the stacked weight is query head
+  // head, key head head - Hq or value head head - Hq - Hkv
+  const int head = nw / kHead;
   uint16_t *dst;
   int H, hh;
-  if (n_tile < g.Hq) {
-    dst = g.q; H = g.Hq; hh = n_tile;
-  } else if (n_tile < g.Hq + g.Hkv) {
-    dst = g.k; H = g.Hkv; hh = n_tile - g.Hq;
+  if (head < g.Hq) {
+    dst = g.q; H = g.Hq; hh = head;
+  } else if (head < g.Hq + g.Hkv) {
+    dst = g.k; H = g.Hkv; hh = head - g.Hq;
   } else {
-    dst = g.v; H = g.Hkv; hh = n_tile - g.Hq - g.Hkv;
+    dst = g.v; H = g.Hkv; hh = head - g.Hq - g.Hkv;
   }
-  const bool rotate = n_tile < g.Hq + g.Hkv;
+  const bool rotate = head < g.Hq + g.Hkv;
   // this lane's pairs are i = 16j + 4(l/16) + e, j, e < 4
   double f[4][4];
   if (rotate) {
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wv + 16 * i + r;
+    const int m = m0 + 64 * wm + 16 * i + r;
     if (m >= g.M) continue;
     f32x4 o[8];
 #pragma unroll
@@ -235,18 +236,138 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
           o[j + 4][e] = x2 * c + x1 * s;
         }
     }
-    uint16_t *dr = dst + ((int64_t)m * H + hh) * kBN + 4 * gq;
+    uint16_t *dr = dst + ((int64_t)m * H + hh) * kHead + 4 * gq;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<u32x2 *>(dr + 16 * j) = u32x2{pack_bf16(o[j][0], o[j][1]), pack_bf16(o[j][2], o[j][3])};
   }
 }
 
+// Few rows (M <= 64, a decode step): the product is bound by streaming the
+// weights, so the work is cut finer.  Workgroup b takes 32 features --
+// 16 of head b / 4 starting at 16 (b % 4) and their RoPE partners 64
+// further -- for all rows; its four wavefronts each take a quarter of the
+// inner dimension, loading their MFMA operands straight from memory (the
+// weights once, the few rows from L2), four 32-deep steps in flight, and
+// the quarters are summed through LDS.  Same D^T = W X^T layout as above,
+// with j = 0 the first 16 features and j = 1 their partners.
+constexpr int kSkinnyRows = 64;
+constexpr int kSkinnyAhead = 4;
+
+template <bool kRope>
+__global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
+  __shared__ __attribute__((aligned(16))) float red[3][64][32];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
+  const int f0 = kHead * (b >> 2) + 16 * (b & 3);  // first feature; partners at f0 + 64
+  const int kq = g.K / 4, kbeg = wv * kq;
+  const uint16_t *wrow[2] = {g.w + (int64_t)(f0 + r) * g.K + 8 * gq, g.w + (int64_t)(f0 + 64 + r) * g.K + 8 * gq};
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load_step = [&](int k, u32x4 (&wa)[2], u32x4 (&xb)[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) wa[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[j] + k));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * i + r;
+      xb[i] = m < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)m * g.K + k + 8 * gq) : u32x4{0, 0, 0, 0};
+    }
+  };
+  const int nsteps = kq / 32;
+  u32x4 wa[kSkinnyAhead][2], xb[kSkinnyAhead][4];
+#pragma unroll
+  for (int a = 0; a < kSkinnyAhead; ++a)
+    if (a < nsteps) load_step(kbeg + 32 * a, wa[a], xb[a]);
+  for (int s0 = 0; s0 < nsteps; s0 += kSkinnyAhead) {
+#pragma unroll
+    for (int a = 0; a < kSkinnyAhead; ++a) {
+      const int st = s0 + a;
+      if (st < nsteps) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma(wa[a][j], xb[a][i], acc[i][j]);
+        if (st + kSkinnyAhead < nsteps) load_step(kbeg + 32 * (st + kSkinnyAhead), wa[a], xb[a]);
+      }
+    }
+  }
+  // sum the four quarters: wavefronts 1-3 park theirs in LDS, wavefront 0 adds
+  if (wv > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[wv - 1][16 * i + r][16 * j + 4 * gq + e] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] += red[q][16 * i + r][16 * j + 4 * gq + e];
+
+  uint16_t *dst = g.y;
+  int64_t row_stride = g.N, col0 = f0;
+  bool rotate = false;
+  double f[4];
+  if (kRope) {
+    const int head = f0 / kHead;
+    int H, hh;
+    if (head < g.Hq) {
+      dst = g.q; H = g.Hq; hh = head;
+    } else if (head < g.Hq + g.Hkv) {
+      dst = g.k; H = g.Hkv; hh = head - g.Hq;
+    } else {
+      dst = g.v; H = g.Hkv; hh = head - g.Hq - g.Hkv;
+    }
+    row_stride = (int64_t)H * kHead;
+    col0 = (int64_t)hh * kHead + (f0 % kHead);
+    rotate = head < g.Hq + g.Hkv;
+    if (rotate) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = rope_turns_per_pos(16 * (b & 3) + 4 * gq + e, g.rope_log2_step);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 16 * i + r;
+    if (m >= g.M) continue;
+    f32x4 o0 = acc[i][0], o1 = acc[i][1];
+    if (kRope && rotate) {
+      const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float c, sn;
+        rope_cos_sin(p, f[e], c, sn);
+        o0[e] = acc[i][0][e] * c - acc[i][1][e] * sn;
+        o1[e] = acc[i][1][e] * c + acc[i][0][e] * sn;
+      }
+    }
+    uint16_t *dr = dst + (int64_t)m * row_stride + col0 + 4 * gq;
+    *reinterpret_cast<u32x2 *>(dr) = u32x2{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
+    *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+  }
+}
+
 inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s); }
 
 int launch_linear(LinearArgs g, bool rope, pkv_stream_t stream) {
+  if (g.M <= kSkinnyRows && g.K % 128 == 0) {
+    const dim3 grid((unsigned)(g.N / 32));
+    if (rope)
+      hipLaunchKernelGGL(linear_skinny_kernel<true>, grid, dim3(256), 0, as_stream(stream), g);
+    else
+      hipLaunchKernelGGL(linear_skinny_kernel<false>, grid, dim3(256), 0, as_stream(stream), g);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+  }
   g.tiles_m = (g.M + kBM - 1) / kBM;
-  const int64_t tiles = (int64_t)g.tiles_m * (g.N / kBN);
+  const int64_t tiles = (int64_t)g.tiles_m * ((g.N + kBN - 1) / kBN);
   if (tiles == 0) return PKV_OK;
   g.tiles_per_xcd = (int32_t)((tiles + kXcds - 1) / kXcds);
   if ((int64_t)g.tiles_per_xcd * kXcds > INT32_MAX) return PKV_ERANGE;
@@ -265,7 +386,7 @@ extern "C" {
 int pkv_linear(const pkv_bf16 *x, const pkv_bf16 *w, int32_t M, int32_t N, int32_t K, pkv_bf16 *y,
                pkv_stream_t stream) {
   if (M < 0 || N < 0 || K < 0) return PKV_EINVAL;
-  if (N % kBN != 0 || K % kBK != 0) return PKV_EUNSUPPORTED;
+  if (N % kHead != 0 || K % kBK != 0) return PKV_EUNSUPPORTED;
   if (M == 0 || N == 0) return PKV_OK;
   if (K == 0) return PKV_EUNSUPPORTED;
   if (!x || !w || !y) return PKV_EINVAL;
