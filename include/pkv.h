@@ -309,7 +309,8 @@ int pkv_qkv_rope(const pkv_bf16 *x, const pkv_bf16 *w_qkv, int32_t num_rows, int
  * y = attn w_o^T with pkv_linear.  w_o: device bf16[hidden][Hq * 128].
  * The caller provides q, k_new, v_new (as above) and attn bf16[T][Hq][128];
  * y: bf16[T][hidden].  The plan, workspace, pools and metadata are those of
- * pkv_paged_step.  Errors: those of the three calls.
+ * pkv_paged_step.  hidden must be a multiple of 128 (PKV_EUNSUPPORTED
+ * before anything is launched).  Errors: those of the three calls.
  * ------------------------------------------------------------------------- */
 int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *w_o, int32_t hidden,
                       pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q, const int32_t *seq_lens,

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
 // the quarters are summed through LDS.  Same D^T = W X^T layout as above,
 // with j = 0 the first 16 features and j = 1 their partners.
 constexpr int kSkinnyRows = 64;
-constexpr int kSkinnyAhead = 4;
+constexpr int kSkinnyAhead = 8;
 
 template <bool kRope>
 __global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
@@ -265,32 +265,43 @@ __global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
   f32x4 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // rows past M read row M - 1 (their results are never stored), so every
+  // load is unconditional and the loads of kSkinnyAhead steps stay in flight
+  const uint16_t *xrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xrow[i] = g.x + (int64_t)min(16 * i + r, g.M - 1) * g.K + 8 * gq;
   auto load_step = [&](int k, u32x4 (&wa)[2], u32x4 (&xb)[4]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) wa[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[j] + k));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * i + r;
-      xb[i] = m < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)m * g.K + k + 8 * gq) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const u32x4 *>(xrow[i] + k);
+  };
+  auto mma = [&](const u32x4 (&wa)[2], const u32x4 (&xb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma(wa[j], xb[i], acc[i][j]);
   };
   const int nsteps = kq / 32;
+  const int ngroups = nsteps / kSkinnyAhead;
   u32x4 wa[kSkinnyAhead][2], xb[kSkinnyAhead][4];
+  if (ngroups > 0) {
 #pragma unroll
-  for (int a = 0; a < kSkinnyAhead; ++a)
-    if (a < nsteps) load_step(kbeg + 32 * a, wa[a], xb[a]);
-  for (int s0 = 0; s0 < nsteps; s0 += kSkinnyAhead) {
+    for (int a = 0; a < kSkinnyAhead; ++a) load_step(kbeg + 32 * a, wa[a], xb[a]);
+    // every group but the last: use each slot, then refill it one group on
+    for (int gi = 0; gi + 1 < ngroups; ++gi) {
 #pragma unroll
-    for (int a = 0; a < kSkinnyAhead; ++a) {
-      const int st = s0 + a;
-      if (st < nsteps) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma(wa[a][j], xb[a][i], acc[i][j]);
-        if (st + kSkinnyAhead < nsteps) load_step(kbeg + 32 * (st + kSkinnyAhead), wa[a], xb[a]);
+      for (int a = 0; a < kSkinnyAhead; ++a) {
+        mma(wa[a], xb[a]);
+        load_step(kbeg + 32 * ((gi + 1) * kSkinnyAhead + a), wa[a], xb[a]);
       }
     }
+#pragma unroll
+    for (int a = 0; a < kSkinnyAhead; ++a) mma(wa[a], xb[a]);
+  }
+  for (int st = ngroups * kSkinnyAhead; st < nsteps; ++st) {
+    load_step(kbeg + 32 * st, wa[0], xb[0]);
+    mma(wa[0], xb[0]);
   }
   // sum the four quarters: wavefronts 1-3 park theirs in LDS, wavefront 0 adds
   if (wv > 0) {
@@ -434,6 +445,10 @@ int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *
                       pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new, pkv_bf16 *attn, pkv_bf16 *y,
                       pkv_stream_t stream) {
   if (!plan) return PKV_EINVAL;
+  // the output projection's features are the hidden size: checked before
+  // anything is launched
+  if (hidden <= 0 || hidden % kHead != 0) return PKV_EUNSUPPORTED;
+  if ((plan->num_q_heads * pkv::kHeadDim) % kBK != 0) return PKV_EUNSUPPORTED;
   int st = pkv_qkv_rope(x, w_qkv, plan->num_rows, hidden, cu_seqlens_q, seq_lens, plan->num_seqs,
                         plan->num_q_heads, plan->num_kv_heads, rope_theta, q, k_new, v_new, stream);
   if (st != PKV_OK) return st;
