@@ -45,15 +45,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 256;              // rows per tile
+constexpr int kBMMax = 256;           // rows per tile, largest form (64 per row wavefront)
 constexpr int kBN = 256;              // features per tile (two heads of 128)
 constexpr int kHead = 128;            // features per wavefront (one head)
 constexpr int kBK = 64;               // inner dimension per stage
 constexpr int kRow = kBK + 8;         // LDS row pitch, bf16: 144 bytes, so the 16 rows of a
                                       // fragment read start in 16 different bank quads
-constexpr int kStage = (kBM + kBN) * kRow;  // bf16 per stage buffer
+constexpr int kStage = (kBMMax + kBN) * kRow;  // bf16 per stage buffer (largest form)
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;
+constexpr int kCUs = 256;             // compute units of an MI355X
 
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -108,8 +109,15 @@ __device__ inline void rope_cos_sin(double p, double f, float &c, float &s) {
   s = __sinf(a);
 }
 
-template <bool kRope>
+// kWaveRows rows per wavefront: 64 (tiles of 256 rows) when there are rows
+// enough to fill the chip with tiles, else 32 (tiles of 128 rows, twice the
+// workgroups for the same work, at more LDS reads per product).
+template <bool kRope, int kWaveRows>
 __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
+  constexpr int kBM = 4 * kWaveRows;
+  constexpr int kRowTiles = kWaveRows / 16;
+  constexpr int kStageT = (kBM + kBN) * kRow;
+  constexpr int kXPieces = kBM * 8 / kThreads;  // 16-byte pieces of the row tile per thread
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
   // blocks go to the XCDs in turn: XCD x takes tiles x * tiles_per_xcd ..,
   // rows fastest, so the blocks resident on one XCD share their weight tile
@@ -119,36 +127,44 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   const int n_tile = t / g.tiles_m, m_tile = t % g.tiles_m;
   const int m0 = m_tile * kBM, n0 = n_tile * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
-  // wavefront wv: rows 64 (wv % 4) .., features (head) 128 (wv / 4) ..
+  // wavefront wv: rows kWaveRows (wv % 4) .., features (head) 128 (wv / 4) ..
   const int wm = wv & 3, wn = wv >> 2;
 
   // Stage loads: thread tid moves 16-byte pieces c = tid + 512u, row c / 8,
-  // column piece c % 8 -- four of the row tile (rows past M read as zero)
-  // and four of the weight tile (rows past N read as zero).
-  u32x4 px[4], pw[4];
+  // column piece c % 8 -- of the row tile (rows past M read as zero) and
+  // four of the weight tile (rows past N read as zero).
+  u32x4 px[kXPieces], pw[4];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kXPieces; ++u) {
       const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
       px[u] = m0 + row < g.M ? *reinterpret_cast<const u32x4 *>(g.x + (int64_t)(m0 + row) * g.K + k0 + 8 * col)
                              : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
       pw[u] = n0 + row < g.N ? *reinterpret_cast<const u32x4 *>(g.w + (int64_t)(n0 + row) * g.K + k0 + 8 * col)
                              : u32x4{0, 0, 0, 0};
     }
   };
   auto stash = [&](int buf) {
-    uint16_t *xs = lds + buf * kStage, *ws = xs + kBM * kRow;
+    uint16_t *xs = lds + buf * kStageT, *ws = xs + kBM * kRow;
+#pragma unroll
+    for (int u = 0; u < kXPieces; ++u) {
+      const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
+      *reinterpret_cast<u32x4 *>(xs + row * kRow + 8 * col) = px[u];
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + kThreads * u, row = c >> 3, col = c & 7;
-      *reinterpret_cast<u32x4 *>(xs + row * kRow + 8 * col) = px[u];
       *reinterpret_cast<u32x4 *>(ws + row * kRow + 8 * col) = pw[u];
     }
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[kRowTiles][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -159,18 +175,18 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   for (int s = 0; s < nk; ++s) {
     const int buf = s & 1;
     if (s + 1 < nk) fetch((s + 1) * kBK);
-    const uint16_t *xs = lds + buf * kStage, *ws = xs + kBM * kRow;
+    const uint16_t *xs = lds + buf * kStageT, *ws = xs + kBM * kRow;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      u32x4 wf[8], xf[4];
+      u32x4 wf[8], xf[kRowTiles];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         wf[j] = *reinterpret_cast<const u32x4 *>(ws + (kHead * wn + 16 * j + r) * kRow + 32 * sub + 8 * gq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        xf[i] = *reinterpret_cast<const u32x4 *>(xs + (64 * wm + 16 * i + r) * kRow + 32 * sub + 8 * gq);
+      for (int i = 0; i < kRowTiles; ++i)
+        xf[i] = *reinterpret_cast<const u32x4 *>(xs + (kWaveRows * wm + 16 * i + r) * kRow + 32 * sub + 8 * gq);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma(wf[j], xf[i], acc[i][j]);
     }
@@ -183,8 +199,8 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   if (nw >= g.N) return;           // past N (N an odd multiple of 128)
   if (!kRope) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 64 * wm + 16 * i + r;
+    for (int i = 0; i < kRowTiles; ++i) {
+      const int m = m0 + kWaveRows * wm + 16 * i + r;
       if (m >= g.M) continue;
       uint16_t *yr = g.y + (int64_t)m * g.N + nw + 4 * gq;
 #pragma unroll
@@ -217,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
       for (int e = 0; e < 4; ++e) f[j][e] = rope_turns_per_pos(16 * j + 4 * gq + e, g.rope_log2_step);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r;
+  for (int i = 0; i < kRowTiles; ++i) {
+    const int m = m0 + kWaveRows * wm + 16 * i + r;
     if (m >= g.M) continue;
     f32x4 o[8];
 #pragma unroll
@@ -377,16 +393,28 @@ int launch_linear(LinearArgs g, bool rope, pkv_stream_t stream) {
       hipLaunchKernelGGL(linear_skinny_kernel<false>, grid, dim3(256), 0, as_stream(stream), g);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
-  g.tiles_m = (g.M + kBM - 1) / kBM;
-  const int64_t tiles = (int64_t)g.tiles_m * ((g.N + kBN - 1) / kBN);
+  // 256-row or 128-row tiles, whichever takes fewer rounds of one
+  // workgroup per CU, a 128-row tile costing ~0.6 of a 256-row one (half
+  // the products at more LDS reads per product, measured on MI355X)
+  const int64_t tiles_n = (g.N + kBN - 1) / kBN;
+  const int64_t rounds_big = ((g.M + 255) / 256 * tiles_n + kCUs - 1) / kCUs;
+  const int64_t rounds_small = ((g.M + 127) / 128 * tiles_n + kCUs - 1) / kCUs;
+  const bool big = 10 * rounds_big <= 6 * rounds_small;
+  const int bm = big ? 256 : 128;
+  g.tiles_m = (g.M + bm - 1) / bm;
+  const int64_t tiles = (int64_t)g.tiles_m * tiles_n;
   if (tiles == 0) return PKV_OK;
   g.tiles_per_xcd = (int32_t)((tiles + kXcds - 1) / kXcds);
   if ((int64_t)g.tiles_per_xcd * kXcds > INT32_MAX) return PKV_ERANGE;
   const dim3 grid((unsigned)(g.tiles_per_xcd * kXcds));
-  if (rope)
-    hipLaunchKernelGGL(linear_kernel<true>, grid, dim3(kThreads), 0, as_stream(stream), g);
+  if (rope && big)
+    hipLaunchKernelGGL((linear_kernel<true, 64>), grid, dim3(kThreads), 0, as_stream(stream), g);
+  else if (rope)
+    hipLaunchKernelGGL((linear_kernel<true, 32>), grid, dim3(kThreads), 0, as_stream(stream), g);
+  else if (big)
+    hipLaunchKernelGGL((linear_kernel<false, 64>), grid, dim3(kThreads), 0, as_stream(stream), g);
   else
-    hipLaunchKernelGGL(linear_kernel<false>, grid, dim3(kThreads), 0, as_stream(stream), g);
+    hipLaunchKernelGGL((linear_kernel<false, 32>), grid, dim3(kThreads), 0, as_stream(stream), g);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
