@@ -19,8 +19,9 @@
 // MFMA operand is one 16-byte piece of a row.  A workgroup of eight
 // wavefronts (two per SIMD, so one's matrix work hides the other's LDS
 // reads) computes a tile of 256 rows x 256 features (two heads) in 64-deep
-// stages staged through LDS (double buffered, the next stage's global loads
-// in flight while the current one is multiplied); wavefront w owns rows
+// stages staged through LDS (double buffered: the next stage's global loads
+// are issued as the current one starts and stored to the other buffer after
+// its first 32-deep half); wavefront w owns rows
 // 64 (w % 4) .. +63 and the 128 features of head w / 4, as D^T = W X^T with
 // v_mfma_f32_16x16x32_bf16:
 //   A operand (features): lane l holds W[16j + l%16][8(l/16) .. +7]
@@ -189,9 +190,11 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
       for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma(wf[j], xf[i], acc[i][j]);
+      // the next stage goes into the other buffer (last read before the
+      // previous barrier) while the second half's products run: measured
+      // 7-8% faster than storing it after both halves
+      if (sub == 0 && s + 1 < nk) stash(buf ^ 1);
     }
-    // the other buffer was last read before the previous barrier
-    if (s + 1 < nk) stash(buf ^ 1);
     __syncthreads();
   }
 
