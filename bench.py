@@ -56,6 +56,8 @@ def parse():
     p.add_argument("--layer-batch", default="mixed", choices=sorted(WORKLOADS),
                    help="layer workload: the step whose rows the layer runs on")
     p.add_argument("--layers", type=int, default=32, help="trace workload: layers per step")
+    p.add_argument("--trace-step-index", type=int, default=150,
+                   help="tracestep workload: which step of the scheduler's trace to time")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true",
                    help="skip the 1 GiB read that evicts L2 and the Infinity Cache before each timed step")
@@ -123,17 +125,18 @@ def kernel_source_sha256() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, batch_name: str):
     """HBM bytes per attention launch from the committed rocprofv3 --pmc
     record for this workload (FETCH_SIZE and WRITE_SIZE, each scaled by the
     factor a plain copy kernel of known size gives), or None when there is
-    no record or the kernel source has changed since it was taken."""
+    no record, the record is of another batch (another trace step), or the
+    kernel source has changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"attention_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256() or rec.get("workload") != batch_name:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -178,7 +181,8 @@ def main():
         return
     dev = torch.device("cuda", 0)
     pkv.load_library()
-    batch = getattr(wl, WORKLOADS[args.workload])()
+    kw = {"index": args.trace_step_index} if args.workload == "tracestep" else {}
+    batch = getattr(wl, WORKLOADS[args.workload])(**kw)
     log(f"workload {batch.name}: {batch.num_seqs} seqs, {batch.num_rows} rows, {batch.num_blocks} blocks")
     t = to_device(batch, dev)
     stream = torch.cuda.current_stream(dev)
@@ -238,7 +242,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
     kernel = "attention_mixed_kernel" if plan.num_wide_items > 0 else "attention_kernel"
-    roof.update({"traffic": measured_traffic(args.workload), "kernel": kernel, "avg_ms": round(attn_ms, 5),
+    roof.update({"traffic": measured_traffic(args.workload, batch.name), "kernel": kernel, "avg_ms": round(attn_ms, 5),
                  "bytes_per_launch": launch_bytes, "flop_per_launch": flop})
 
     cpu = None

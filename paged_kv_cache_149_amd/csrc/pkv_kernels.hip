@@ -577,10 +577,11 @@ __device__ __forceinline__ WideTile wide_tile(const AttnArgs &a, int idx) {
   return d;
 }
 
-// A column's scores may exceed its reference by this much (log2 units):
-// probabilities stay below 2^100 and their sums (at most 2^31 keys) finite
-// in fp32.  A wavefront with a column past it recomputes its columns.
-constexpr float kRedoLog2 = 100.f;
+// A column's probabilities (relative to its reference) may sum to this
+// much: every one of them, and every output accumulator, then stays finite
+// in fp32 (|v| < 2^27).  A wavefront with a column sum past it, or not
+// finite, recomputes its columns.
+constexpr float kRedoSum = 0x1p100f;
 
 // The wide tiles items[i0, i1) of one persistent workgroup.
 __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1) {
@@ -717,19 +718,18 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     // Probabilities are taken relative to a fixed per-column reference: the
     // column's maximum score in the tile's first chunk (key 0 is in it).
     // fp32 and bf16 keep 8 exponent bits, so later scores may exceed it by
-    // up to kRedoLog2 without overflow and nothing is rescaled -- the
-    // accumulators never leave the matrix cores inside the loop.  Each lane
-    // tracks the largest raw score it sees; a wavefront with a column past
-    // the margin recomputes its columns after the list (exactly, with the
-    // running-maximum softmax of the narrow path).
+    // up to 100 (log2 units) without overflow and nothing is rescaled -- the
+    // accumulators never leave the matrix cores inside the loop.  Past the
+    // first chunk no maximum is tracked: a probability above kRedoSum makes
+    // its column's sum exceed it too, so a wavefront with a column sum past
+    // kRedoSum (or not finite) recomputes its columns after the list
+    // (exactly, with the running-maximum softmax of the narrow path).
     f32x4 acc[NT][8];
     float neg_ref[NT];  // -(reference) in log2 units
-    float m_hi[NT];     // this lane's largest raw score
     float l_part[NT];   // this lane's sum of its rounded probabilities
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       l_part[nt] = 0.f;
-      m_hi[nt] = neg_inf();
       neg_ref[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[nt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -807,16 +807,13 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
             sv[nt][j] = (col_ok[nt] && key < d.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
           }
       }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        m_hi[nt] = max3(max3(max3(m_hi[nt], sv[nt][0], sv[nt][1]), max3(sv[nt][2], sv[nt][3], sv[nt][4]),
-                             sv[nt][5]),
-                        sv[nt][6], sv[nt][7]);
       if (c == 0) {
         // the reference: the column's maximum over the first chunk
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float mx = xmax32(xmax16(m_hi[nt]));
+          const float m = max3(max3(sv[nt][0], sv[nt][1], sv[nt][2]), max3(sv[nt][3], sv[nt][4], sv[nt][5]),
+                               __builtin_fmaxf(sv[nt][6], sv[nt][7]));
+          const float mx = xmax32(xmax16(m));
           neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
         }
       }
@@ -864,21 +861,23 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       phase_m(s);
     }
 
+    // column sums over the four lane groups
+    float l_tot[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
+
     // did a column outgrow its reference?  (rare: recomputed after the list)
     {
       bool grew = false;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) grew |= __builtin_fmaf(m_hi[nt], c2, neg_ref[nt]) > kRedoLog2;
+      for (int nt = 0; nt < NT; ++nt) grew |= !(l_tot[nt] <= kRedoSum);
       if (__builtin_amdgcn_ballot_w64(grew)) {
         if (i - i0 < 64) redo |= 1ull << (i - i0);
         else redo_all = true;
       }
     }
 
-    // epilogue: column sums over the four lane groups, then O / l
-    float l_tot[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
+    // epilogue: O / l
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if (!col_ok[nt]) continue;
