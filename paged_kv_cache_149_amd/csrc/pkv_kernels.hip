@@ -541,9 +541,25 @@ __device__ __forceinline__ void wait_lds_but8_for(u32x4 (&x)[8]) {
 #undef PKV_OPS8
 #undef PKV_DS_READ
 
-// Hands the Q^T operand registers through an empty asm statement: the
-// compiler waits for their loads here, at a fixed point after the step's
-// chunk loads, rather than wherever its loop analysis would put the wait.
+// The Q^T operands of a wide tile are loaded by plain global_load_dwordx4
+// instructions in asm, so the compiler does not place waits for them (its
+// loop analysis would wait for every chunk load in flight); the caller waits
+// with an explicit count and then hands the registers through an empty asm
+// statement, so no use can be scheduled above the wait.  Each register is
+// tied in and out, so the load writes the registers the operands live in.
+#define PKV_GLOAD(x, off) asm volatile("global_load_dwordx4 %0, %1, off offset:" #off : "+v"(x) : "v"(p) : "memory")
+template <int NT>
+__device__ __forceinline__ void q_load(u32x4 (&q)[NT][4], const uint16_t *const (&ptr)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint16_t *p = ptr[nt];
+    PKV_GLOAD(q[nt][0], 0);
+    PKV_GLOAD(q[nt][1], 64);
+    PKV_GLOAD(q[nt][2], 128);
+    PKV_GLOAD(q[nt][3], 192);
+  }
+}
+#undef PKV_GLOAD
 template <int NT>
 __device__ __forceinline__ void q_ready(u32x4 (&q)[NT][4]) {
 #pragma unroll
@@ -685,9 +701,41 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
   uint64_t redo = 0;     // list positions < 64 whose columns need recomputing
   bool redo_all = false; // a later position does (recompute every tile)
   WideTile dn = wide_tile(a, i0);  // the next tile's descriptor, fetched a tile ahead
+
+  // Q^T operands of a tile; columns past the tile read the zero tile.  The
+  // next tile's are loaded as soon as the last S^T tiles of the current one
+  // have been issued, so they land during its last steps and epilogue, and
+  // waiting for them does not wait for the chunk loads issued after them.
+  // q_mark: the stream's issue count when they were issued.
+  u32x4 qb[NT][4];
+  for (int nt = 0; nt < NT; ++nt)
+    for (int c = 0; c < 4; ++c) qb[nt][c] = u32x4{0u, 0u, 0u, 0u};
+  int q_mark = 0;
+  const uint16_t *qnext[NT];  // this lane's Q^T operand addresses in the next tile
+  auto q_addresses = [&](const WideTile &t) {
+    const int tnp = max(0, min(WP, t.np - w * WP));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int col = nt * 16 + r;
+      const int pc = col >> a.log2G;
+      qnext[nt] =
+          (pc < tnp ? a.q + ((int64_t)(t.t0 + w * WP + pc) * a.Hq + t.kvh * G + (col & (G - 1))) * D : a.zero) +
+          8 * g;
+    }
+  };
+  auto load_q = [&]() {
+    q_load(qb, qnext);
+    q_mark = n_issued;
+  };
+  q_addresses(dn);
+  load_q();
   for (int i = i0; i < i1; ++i) {
     const WideTile d = dn;
-    if (i + 1 < i1) dn = wide_tile(a, i + 1);
+    const bool next_q = i + 1 < i1;
+    if (next_q) {
+      dn = wide_tile(a, i + 1);
+      q_addresses(dn);
+    }
     const int wpos0 = d.pos0 + w * WP;  // first position of this wavefront
     const int wnp = max(0, min(WP, d.np - w * WP));
     const int wlast = wpos0 + wnp - 1;
@@ -704,15 +752,6 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       col_ok[nt] = pc < wnp;
       col_pos[nt] = wpos0 + pc;
       col_qoff[nt] = ((int64_t)(d.t0 + w * WP + pc) * a.Hq + d.kvh * G + ho) * D;
-    }
-    // Q^T operands; columns past the tile read the zero tile (no branch, so
-    // the loads' registers are never written by anything else)
-    u32x4 qb[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint16_t *qp = (col_ok[nt] ? a.q + col_qoff[nt] : a.zero) + 8 * g;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qb[nt][c] = load16(qp + 32 * c);
     }
 
     // Probabilities are taken relative to a fixed per-column reference: the
@@ -829,19 +868,45 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
 
     // Each step: every LDS read of this wavefront is done (its slot may be
     // refilled) and its loads of the tile's chunk s have landed -- the
-    // stream's next kAhead - 1 chunks, issued after it, may still fly.  The
-    // issue of chunk s is followed by exactly kLoadsPerIssue loads per later
-    // chunk (and, at step 0, by the Q loads, which the wait then also
-    // covers).
+    // stream's next kAhead - 1 chunks, issued after it, may still fly.
+    // Loads complete in order, so the count to wait for is the loads issued
+    // after the chunk's: kLoadsPerIssue per later chunk, plus the latest Q
+    // loads when they came later (earlier Q loads left uncounted only make
+    // the wait stricter; stores never make it weaker).
     auto wait_chunk = [&](int s) {
       wait_lds();
-      switch (n_issued - 1 - (g_base + s)) {
-        case 4: wait_vmcnt<4 * kLoadsPerIssue>(); break;
-        case 3: wait_vmcnt<3 * kLoadsPerIssue>(); break;
-        case 2: wait_vmcnt<2 * kLoadsPerIssue>(); break;
-        case 1: wait_vmcnt<kLoadsPerIssue>(); break;
+      static_assert(kLoadsPerIssue * (kAhead - 1) + 4 * NT == 16, "wait counts below");
+      const int later = n_issued - 1 - (g_base + s);
+      const bool q_later = q_mark > g_base + s;
+      if (__builtin_expect(later == kAhead - 1 && !q_later, 1)) {  // the steady state
+        wait_vmcnt<kLoadsPerIssue * (kAhead - 1)>();
+        return;
+      }
+      switch (kLoadsPerIssue * later + (q_later ? 4 * NT : 0)) {
+        case 16: wait_vmcnt<16>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 2: wait_vmcnt<2>(); break;
         default: wait_vmcnt<0>(); break;
       }
+    };
+    // the tile's Q loads have landed: every load issued after them may fly
+    auto wait_q = [&]() {
+      switch (n_issued - q_mark) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<kLoadsPerIssue>(); break;
+        case 2: wait_vmcnt<2 * kLoadsPerIssue>(); break;
+        case 3: wait_vmcnt<3 * kLoadsPerIssue>(); break;
+        case 4: wait_vmcnt<4 * kLoadsPerIssue>(); break;
+        case 5: wait_vmcnt<5 * kLoadsPerIssue>(); break;
+        case 6: wait_vmcnt<6 * kLoadsPerIssue>(); break;
+        default: wait_vmcnt<7 * kLoadsPerIssue>(); break;
+      }
+      q_ready(qb);
     };
     // step 0 (a tile has at least one chunk)
     wait_chunk(0);
@@ -849,9 +914,11 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     issue_next();
     phase_v(-1);
     barrier();
-    q_ready(qb);
+    wait_q();
     phase_m(0);
+    const int s_next_q = next_q ? max(ncomp, 1) : -1;  // after the tile's last S^T tiles (phase_m(ncomp - 1))
     for (int s = 1; s <= d.nch; ++s) {
+      if (s == s_next_q) load_q();
       if (s < d.nch) wait_chunk(s);
       else wait_lds();
       barrier();
