@@ -30,6 +30,7 @@
 // their operands straight from HBM in MFMA layout; wide tiles stage each
 // chunk once per workgroup in LDS, in the same layout.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include <algorithm>
 
@@ -650,10 +651,14 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
   WideTile nd = i0 + 1 < i1 ? wide_tile(a, i0 + 1) : cd;
   int b0, b1;
   auto fetch_ids = [&]() {
+    // both loads always issue (clamped to the tile's last entry, kb_end >= 1),
+    // so the stream's steps have no branches around them
     const int32_t *btrow = a.bt + (int64_t)cd.seq * a.bt_stride;
     const bool live = ci < i1;
-    b0 = live && 2 * ccc < cd.kb_end ? sload(btrow, 2 * ccc) : -1;
-    b1 = live && 2 * ccc + 1 < cd.kb_end ? sload(btrow, 2 * ccc + 1) : -1;
+    const int32_t e0 = sload(btrow, min(2 * ccc, cd.kb_end - 1));
+    const int32_t e1 = sload(btrow, min(2 * ccc + 1, cd.kb_end - 1));
+    b0 = live && 2 * ccc < cd.kb_end ? e0 : -1;
+    b1 = live && 2 * ccc + 1 < cd.kb_end ? e1 : -1;
   };
   fetch_ids();
   auto issue_next = [&]() {
@@ -777,9 +782,12 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     f32x4 sc[NT][2];
     u32x4 pb[NT];
 
-    auto phase_m = [&](int c) {
-      const bool do_qk = c >= 0 && c < ncomp;
-      const bool do_pv = c >= 1 && c - 1 < ncomp;
+    // kSteady: 1 <= c - 1, c < ncomp and chunk c - 1 needs no masking (the
+    // caller's range guarantees it), so the conditions fold away.
+    auto phase_m = [&](int c, auto steady) {
+      constexpr bool kSteady = decltype(steady)::value;
+      const bool do_qk = kSteady || (c >= 0 && c < ncomp);
+      const bool do_pv = kSteady || (c >= 1 && c - 1 < ncomp);
       if (!do_qk && !do_pv) return;
       __builtin_amdgcn_s_setprio(1);
       // the V^T operands of chunk c-1 land while the S^T tiles are computed
@@ -803,7 +811,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       if (do_pv) {
         wait_lds_for(vop);
         const int key0 = 32 * (c - 1);
-        if (key0 + 32 > d.k1) {
+        if (!kSteady && key0 + 32 > d.k1) {
           // keys past the tile may hold stale data: zero their values
           const int nv = d.k1 - (key0 + 8 * g);
           u32x4 keep;
@@ -821,10 +829,12 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       __builtin_amdgcn_s_setprio(0);
     };
 
-    auto phase_v = [&](int c) {
+    // kSteady: 1 <= c, c + 1 < ncomp and chunk c needs no masking
+    auto phase_v = [&](int c, auto steady) {
+      constexpr bool kSteady = decltype(steady)::value;
       // reads for the next matrix phase first, so they land during the softmax
-      if (c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(g_base + c + 1), lane), kop);
-      if (c < 0 || c >= ncomp) return;
+      if (kSteady || c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(g_base + c + 1), lane), kop);
+      if (!kSteady && (c < 0 || c >= ncomp)) return;
       const int key0 = 32 * c;
       const int kl = key0 + 8 * g;
       float sv[NT][8];
@@ -837,7 +847,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         }
       // causal masking is needed only where a key can lie past a column's
       // position (or past the tile, or on empty columns)
-      if (key0 + 31 > wpos0 || wnp < WP || key0 + 32 > d.k1) {
+      if (!kSteady && (key0 + 31 > wpos0 || wnp < WP || key0 + 32 > d.k1)) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -846,7 +856,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
             sv[nt][j] = (col_ok[nt] && key < d.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
           }
       }
-      if (c == 0) {
+      if (!kSteady && c == 0) {
         // the reference: the column's maximum over the first chunk
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -875,23 +885,14 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     // the wait stricter; stores never make it weaker).
     auto wait_chunk = [&](int s) {
       wait_lds();
+      // every step issues one chunk, so kAhead - 1 chunks were issued after
+      // chunk s; anything else (not expected) waits for everything
       static_assert(kLoadsPerIssue * (kAhead - 1) + 4 * NT == 16, "wait counts below");
-      const int later = n_issued - 1 - (g_base + s);
-      const bool q_later = q_mark > g_base + s;
-      if (__builtin_expect(later == kAhead - 1 && !q_later, 1)) {  // the steady state
-        wait_vmcnt<kLoadsPerIssue * (kAhead - 1)>();
-        return;
-      }
-      switch (kLoadsPerIssue * later + (q_later ? 4 * NT : 0)) {
-        case 16: wait_vmcnt<16>(); break;
-        case 14: wait_vmcnt<14>(); break;
-        case 12: wait_vmcnt<12>(); break;
-        case 10: wait_vmcnt<10>(); break;
-        case 8: wait_vmcnt<8>(); break;
-        case 6: wait_vmcnt<6>(); break;
-        case 4: wait_vmcnt<4>(); break;
-        case 2: wait_vmcnt<2>(); break;
-        default: wait_vmcnt<0>(); break;
+      if (__builtin_expect(n_issued - 1 - (g_base + s) == kAhead - 1, 1)) {
+        if (q_mark > g_base + s) wait_vmcnt<16>();
+        else wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
       }
     };
     // the tile's Q loads have landed: every load issued after them may fly
@@ -908,25 +909,37 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       }
       q_ready(qb);
     };
+    constexpr std::false_type kAny{};
+    constexpr std::true_type kSteadyStep{};
     // step 0 (a tile has at least one chunk)
     wait_chunk(0);
     barrier();
     issue_next();
-    phase_v(-1);
+    phase_v(-1, kAny);
     barrier();
     wait_q();
-    phase_m(0);
+    phase_m(0, kAny);
     const int s_next_q = next_q ? max(ncomp, 1) : -1;  // after the tile's last S^T tiles (phase_m(ncomp - 1))
-    for (int s = 1; s <= d.nch; ++s) {
-      if (s == s_next_q) load_q();
-      if (s < d.nch) wait_chunk(s);
+    auto step = [&](int s, auto steady) {
+      constexpr bool kSteady = decltype(steady)::value;
+      if (!kSteady && s == s_next_q) load_q();
+      if (kSteady || s < d.nch) wait_chunk(s);
       else wait_lds();
       barrier();
-      if (s < d.nch) issue_next();
-      phase_v(s - 1);
+      if (kSteady || s < d.nch) issue_next();
+      phase_v(s - 1, steady);
       barrier();
-      phase_m(s);
-    }
+      phase_m(s, steady);
+    };
+    // Steady steps: s in [2, s_hi) -- chunk s - 1 is neither the first nor
+    // masked (the wavefront has all its positions, every key of the chunk
+    // lies at or before its first position and inside the tile) and chunk s
+    // still has S^T tiles; the other steps take the general path.
+    const int s_hi = wnp < WP ? 0 : min(ncomp, min((wpos0 + 1) >> 5, d.k1 >> 5) + 1);
+    int s = 1;
+    for (; s < min(2, d.nch + 1); ++s) step(s, kAny);
+    for (; s < s_hi; ++s) step(s, kSteadyStep);
+    for (; s <= d.nch; ++s) step(s, kAny);
 
     // column sums over the four lane groups
     float l_tot[NT];
