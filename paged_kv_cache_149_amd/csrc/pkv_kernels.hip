@@ -649,16 +649,18 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
   int ci = i0, ccc = 0, n_issued = 0;
   WideTile cd = wide_tile(a, i0);
   WideTile nd = i0 + 1 < i1 ? wide_tile(a, i0 + 1) : cd;
-  int b0, b1;
+  // The next issue's two table entries (clamped to the tile's last one,
+  // kb_end >= 1, so both loads always issue) and whether each is real; the
+  // selection happens at the issue, so no step waits for these loads.
+  int e0, e1;
+  bool ok0, ok1;
   auto fetch_ids = [&]() {
-    // both loads always issue (clamped to the tile's last entry, kb_end >= 1),
-    // so the stream's steps have no branches around them
     const int32_t *btrow = a.bt + (int64_t)cd.seq * a.bt_stride;
     const bool live = ci < i1;
-    const int32_t e0 = sload(btrow, min(2 * ccc, cd.kb_end - 1));
-    const int32_t e1 = sload(btrow, min(2 * ccc + 1, cd.kb_end - 1));
-    b0 = live && 2 * ccc < cd.kb_end ? e0 : -1;
-    b1 = live && 2 * ccc + 1 < cd.kb_end ? e1 : -1;
+    e0 = sload(btrow, min(2 * ccc, cd.kb_end - 1));
+    e1 = sload(btrow, min(2 * ccc + 1, cd.kb_end - 1));
+    ok0 = live && 2 * ccc < cd.kb_end;
+    ok1 = live && 2 * ccc + 1 < cd.kb_end;
   };
   fetch_ids();
   auto issue_next = [&]() {
@@ -666,17 +668,21 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     auto tile = [&](int b) -> const uint16_t * {
       return (uint32_t)b < nblk ? cache + (uint64_t)((uint32_t)b * (uint32_t)a.Hkv + hoff) * TILE : a.zero;
     };
+    const int b0 = ok0 ? e0 : -1, b1 = ok1 ? e1 : -1;
     const uint16_t *src = (sel ? tile(b1) : tile(b0)) + lane_off;
     u32x4 *dst = slot(n_issued) + w * RPW * 64;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(src + (kside ? kKGroupElems : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0,
                                      0);
     ++n_issued;
-    if (ci < i1 && ++ccc >= cd.nch) {
+    const bool live = ci < i1;
+    if (__builtin_expect(live && ccc + 1 >= cd.nch, 0)) {  // the cursor's tile is done
       ccc = 0;
       ++ci;
       cd = nd;
       if (ci + 1 < i1) nd = wide_tile(a, ci + 1);
+    } else {
+      ++ccc;  // past the list it only feeds clamped, unused table reads
     }
     fetch_ids();
   };
@@ -923,8 +929,17 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     auto step = [&](int s, auto steady) {
       constexpr bool kSteady = decltype(steady)::value;
       if (!kSteady && s == s_next_q) load_q();
-      if (kSteady || s < d.nch) wait_chunk(s);
-      else wait_lds();
+      if (kSteady) {
+        // The tile's Q loads were waited for at step 0 and the next tile's
+        // are not issued yet, so every load issued before them has landed
+        // and only the kAhead - 1 later chunks' loads may still fly.
+        wait_lds();
+        wait_vmcnt<kLoadsPerIssue * (kAhead - 1)>();
+      } else if (s < d.nch) {
+        wait_chunk(s);
+      } else {
+        wait_lds();
+      }
       barrier();
       if (kSteady || s < d.nch) issue_next();
       phase_v(s - 1, steady);
