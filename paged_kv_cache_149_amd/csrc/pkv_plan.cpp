@@ -41,10 +41,11 @@ constexpr int kDefaultWorkgroups = 256;    // one per CU on an MI355X
 constexpr int kXcds = 8;                   // consecutive workgroups go to the XCDs in turn
 
 // Cost model of the launch with wide tiles, in CU-microseconds (measured on
-// MI355X): a wide tile costs ~1.1 us per 32-key chunk plus ~2 us to start;
+// MI355X): a wide tile costs ~0.9 us per 32-key chunk plus ~2 us to start;
 // a narrow workgroup streams its 32-key chunks (16 KiB of K and V) at
-// ~30 GB/s per CU.
-constexpr double kWideChunkUs = 1.1;
+// ~30 GB/s per CU.  (0.9 measured 1-1.5% faster than 1.1 or 0.75 on mixed
+// and trace steps; a larger start cost or another narrow rate, no better.)
+constexpr double kWideChunkUs = 0.9;
 constexpr double kWideTileUs = 2.0;
 constexpr double kNarrowChunkUs = 16384.0 / 30.0e3;
 
