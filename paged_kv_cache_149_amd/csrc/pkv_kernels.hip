@@ -641,9 +641,9 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
   // then all-zero chunks.  The cursor (tile ci, chunk ccc) issues stream
   // chunk n_issued into ring slot n_issued % kNbuf.  Table entries outside
   // [0, num_blocks), blocks past a tile, and the chunks after the list read
-  // the all-zero tile.  The block ids of the next issue (b0, b1) and the
-  // descriptor of the cursor's next tile (nd) are fetched one issue ahead,
-  // so no issue waits on a scalar load.  Every call issues exactly
+  // the all-zero tile.  The table entries of the next issue (e0, e1) and
+  // the descriptor of the cursor's next tile (nd) are fetched one issue
+  // ahead, so no issue waits on a scalar load.  Every call issues exactly
   // kLoadsPerIssue loads, so the loads in flight behind any chunk are known
   // on every path.
   int ci = i0, ccc = 0, n_issued = 0;

@@ -233,6 +233,19 @@ def test_plan_options_same_result(dev, opts):
     check_attention(out, oracle.packed_attention(b), f"options {opts}")
 
 
+@pytest.mark.parametrize("opts", [None, {"workgroups": 8}, {"workgroups": 16, "narrow_waves": 64}])
+def test_wide_lists_with_interior_chunks(dev, opts):
+    """Prefill tiles long enough to have interior (unmasked) chunks beside
+    partial tiles and one-chunk tiles, dealt to few workgroups so one
+    workgroup walks many tiles: every tile's Q operands are loaded while the
+    previous tile finishes, and interior steps take the branch-free path."""
+    seqs = [(300, 70), (0, 200), (1000, 64), (65, 1), (129, 33), (2000, 128), (0, 5), (96, 17)]
+    b = wl.make_batch("wide-lists", seqs, seed=36)
+    note(f"wide lists {opts}")
+    out, _, _, _ = run_step(b, dev, options=opts)
+    check_attention(out, oracle.packed_attention(b), f"wide lists {opts}")
+
+
 def test_nan_in_unused_slots_does_not_leak(dev):
     """Slots past each sequence's end in its last block hold NaN bits."""
     b = wl.make_batch("nan-tail", [(20, 1), (0, 7), (37, 2)], seed=34, pool="materialize")
