@@ -788,12 +788,14 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     f32x4 sc[NT][2];
     u32x4 pb[NT];
 
-    // kSteady: 1 <= c - 1, c < ncomp and chunk c - 1 needs no masking (the
-    // caller's range guarantees it), so the conditions fold away.
+    // kInterior (modes 1 and 2): 1 <= c - 1 and c < ncomp, so both halves
+    // run; mode 1 also has chunk c - 1 free of masking (the caller's range
+    // guarantees either), so the conditions fold away.
     auto phase_m = [&](int c, auto steady) {
-      constexpr bool kSteady = decltype(steady)::value;
-      const bool do_qk = kSteady || (c >= 0 && c < ncomp);
-      const bool do_pv = kSteady || (c >= 1 && c - 1 < ncomp);
+      constexpr bool kSteady = decltype(steady)::value == 1;
+      constexpr bool kInterior = decltype(steady)::value != 0;
+      const bool do_qk = kInterior || (c >= 0 && c < ncomp);
+      const bool do_pv = kInterior || (c >= 1 && c - 1 < ncomp);
       if (!do_qk && !do_pv) return;
       __builtin_amdgcn_s_setprio(1);
       // the V^T operands of chunk c-1 land while the S^T tiles are computed
@@ -835,12 +837,13 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       __builtin_amdgcn_s_setprio(0);
     };
 
-    // kSteady: 1 <= c, c + 1 < ncomp and chunk c needs no masking
+    // kInterior: 1 <= c and c + 1 < ncomp; kSteady: also no masking in chunk c
     auto phase_v = [&](int c, auto steady) {
-      constexpr bool kSteady = decltype(steady)::value;
+      constexpr bool kSteady = decltype(steady)::value == 1;
+      constexpr bool kInterior = decltype(steady)::value != 0;
       // reads for the next matrix phase first, so they land during the softmax
-      if (kSteady || c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(g_base + c + 1), lane), kop);
-      if (!kSteady && (c < 0 || c >= ncomp)) return;
+      if (kInterior || c + 1 < ncomp) lds_read_k(lds_lane_addr(slot(g_base + c + 1), lane), kop);
+      if (!kInterior && (c < 0 || c >= ncomp)) return;
       const int key0 = 32 * c;
       const int kl = key0 + 8 * g;
       float sv[NT][8];
@@ -862,7 +865,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
             sv[nt][j] = (col_ok[nt] && key < d.k1 && key <= col_pos[nt]) ? sv[nt][j] : neg_inf();
           }
       }
-      if (!kSteady && c == 0) {
+      if (!kInterior && c == 0) {
         // the reference: the column's maximum over the first chunk
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -915,8 +918,9 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       }
       q_ready(qb);
     };
-    constexpr std::false_type kAny{};
-    constexpr std::true_type kSteadyStep{};
+    constexpr std::integral_constant<int, 0> kAny{};
+    constexpr std::integral_constant<int, 1> kSteadyStep{};
+    constexpr std::integral_constant<int, 2> kMaskedStep{};
     // step 0 (a tile has at least one chunk)
     wait_chunk(0);
     barrier();
@@ -927,9 +931,9 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     phase_m(0, kAny);
     const int s_next_q = next_q ? max(ncomp, 1) : -1;  // after the tile's last S^T tiles (phase_m(ncomp - 1))
     auto step = [&](int s, auto steady) {
-      constexpr bool kSteady = decltype(steady)::value;
-      if (!kSteady && s == s_next_q) load_q();
-      if (kSteady) {
+      constexpr bool kInterior = decltype(steady)::value != 0;
+      if (!kInterior && s == s_next_q) load_q();
+      if (kInterior) {
         // The tile's Q loads were waited for at step 0 and the next tile's
         // are not issued yet, so every load issued before them has landed
         // and only the kAhead - 1 later chunks' loads may still fly.
@@ -941,7 +945,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         wait_lds();
       }
       barrier();
-      if (kSteady || s < d.nch) issue_next();
+      if (kInterior || s < d.nch) issue_next();
       phase_v(s - 1, steady);
       barrier();
       phase_m(s, steady);
@@ -949,11 +953,14 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     // Steady steps: s in [2, s_hi) -- chunk s - 1 is neither the first nor
     // masked (the wavefront has all its positions, every key of the chunk
     // lies at or before its first position and inside the tile) and chunk s
-    // still has S^T tiles; the other steps take the general path.
+    // still has S^T tiles.  Masked interior steps: s in [s_hi, ncomp), the
+    // same with the masks tested at run time.  The first step and those past
+    // the wavefront's last S^T tiles take the general path.
     const int s_hi = wnp < WP ? 0 : min(ncomp, min((wpos0 + 1) >> 5, d.k1 >> 5) + 1);
     int s = 1;
     for (; s < min(2, d.nch + 1); ++s) step(s, kAny);
     for (; s < s_hi; ++s) step(s, kSteadyStep);
+    for (; s < ncomp; ++s) step(s, kMaskedStep);  // interior steps whose chunk needs masking
     for (; s <= d.nch; ++s) step(s, kAny);
 
     // column sums over the four lane groups
