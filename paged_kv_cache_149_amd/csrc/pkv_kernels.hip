@@ -806,8 +806,13 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         wait_lds_for(kop);
       }
       if (do_qk) {
+        // past the first chunk the accumulators start at -(reference), so
+        // the scores come out of the matrix cores ready for the exponential
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) {
+          const float r0 = kInterior || c >= 1 ? neg_ref[nt] : 0.f;
+          sc[nt][0] = sc[nt][1] = f32x4{r0, r0, r0, r0};
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -872,15 +877,19 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
           const float m = max3(max3(sv[nt][0], sv[nt][1], sv[nt][2]), max3(sv[nt][3], sv[nt][4], sv[nt][5]),
                                __builtin_fmaxf(sv[nt][6], sv[nt][7]));
           const float mx = xmax32(xmax16(m));
-          neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
+          neg_ref[nt] = mx == neg_inf() ? 0.f : -mx;
         }
       }
+      // scores are in log2 units (Q pre-scaled); the first chunk's still
+      // lack the reference
+      const bool first = !kInterior && c == 0;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[nt][e] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * e], c2, neg_ref[nt])),
-                                __builtin_amdgcn_exp2f(__builtin_fmaf(sv[nt][2 * e + 1], c2, neg_ref[nt])));
+          const float x0 = first ? sv[nt][2 * e] + neg_ref[nt] : sv[nt][2 * e];
+          const float x1 = first ? sv[nt][2 * e + 1] + neg_ref[nt] : sv[nt][2 * e + 1];
+          pb[nt][e] = pack_bf16(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
           l_part[nt] = sum_bf16x2(pb[nt][e], l_part[nt]);
         }
     };
@@ -917,6 +926,16 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         default: wait_vmcnt<7 * kLoadsPerIssue>(); break;
       }
       q_ready(qb);
+      // Q scaled by scale * log2(e) and rounded once more to bf16, so the
+      // scores come out of the matrix cores in log2 units (no multiply per
+      // score in the softmax)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            qb[nt][c][e] = pack_bf16(bf16_lo(qb[nt][c][e]) * c2, bf16_hi(qb[nt][c][e]) * c2);
     };
     constexpr std::integral_constant<int, 0> kAny{};
     constexpr std::integral_constant<int, 1> kSteadyStep{};
