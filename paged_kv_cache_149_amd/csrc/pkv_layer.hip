@@ -56,6 +56,7 @@ constexpr int kStage = (kBMMax + kBN) * kRow;  // bf16 per stage buffer (largest
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;             // compute units of an MI355X
+constexpr int kGroupRows = 8;         // row tiles per group of the tile order
 
 __device__ inline f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -124,8 +125,15 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
   // rows fastest, so the blocks resident on one XCD share their weight tile
   const int b = blockIdx.x;
   const int t = (b % kXcds) * g.tiles_per_xcd + b / kXcds;
-  if (t >= g.tiles_m * ((g.N + kBN - 1) / kBN)) return;
-  const int n_tile = t / g.tiles_m, m_tile = t % g.tiles_m;
+  const int tiles_n = (g.N + kBN - 1) / kBN;
+  if (t >= g.tiles_m * tiles_n) return;
+  // tiles in groups of kGroupRows row tiles x every feature tile, rows
+  // fastest: a round of 32 workgroups on one XCD covers 8 row tiles x 4
+  // feature tiles, so each row tile and each weight tile is read by several
+  // workgroups of the XCD at once and mostly hits its L2
+  const int grp = t / (kGroupRows * tiles_n), first_m = grp * kGroupRows;
+  const int gm = min(g.tiles_m - first_m, kGroupRows), in_grp = t % (kGroupRows * tiles_n);
+  const int m_tile = first_m + in_grp % gm, n_tile = in_grp / gm;
   const int m0 = m_tile * kBM, n0 = n_tile * kBN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
   // wavefront wv: rows kWaveRows (wv % 4) .., features (head) 128 (wv / 4) ..
