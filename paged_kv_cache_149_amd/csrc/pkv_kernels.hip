@@ -601,6 +601,13 @@ __device__ __forceinline__ WideTile wide_tile(const AttnArgs &a, int idx) {
 constexpr float kRedoSum = 0x1p100f;
 
 // The wide tiles items[i0, i1) of one persistent workgroup.
+// kPreScaled: Q is multiplied by scale * log2(e) once per tile and rounded
+// to bf16 again, the S^T accumulators start at -(reference), and the
+// softmax needs no multiply per score.  The extra rounding perturbs each
+// log2-domain score by ~2^-9 relative per Q element, so the launch uses this
+// form only at or below the softmax scale 1/sqrt(head_dim); larger scales
+// take the exact form (the scale applied in fp32 in each exponent's FMA).
+template <bool kPreScaled>
 __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1) {
   constexpr int WV = pkv::kWideWaves;
   constexpr int NT = pkv::kWideCols / (16 * WV);  // MFMA column tiles per wavefront
@@ -810,7 +817,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         // the scores come out of the matrix cores ready for the exponential
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float r0 = kInterior || c >= 1 ? neg_ref[nt] : 0.f;
+          const float r0 = kPreScaled && (kInterior || c >= 1) ? neg_ref[nt] : 0.f;
           sc[nt][0] = sc[nt][1] = f32x4{r0, r0, r0, r0};
         }
 #pragma unroll
@@ -877,7 +884,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
           const float m = max3(max3(sv[nt][0], sv[nt][1], sv[nt][2]), max3(sv[nt][3], sv[nt][4], sv[nt][5]),
                                __builtin_fmaxf(sv[nt][6], sv[nt][7]));
           const float mx = xmax32(xmax16(m));
-          neg_ref[nt] = mx == neg_inf() ? 0.f : -mx;
+          neg_ref[nt] = mx == neg_inf() ? 0.f : (kPreScaled ? -mx : -mx * c2);
         }
       }
       // scores are in log2 units (Q pre-scaled); the first chunk's still
@@ -887,8 +894,12 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = first ? sv[nt][2 * e] + neg_ref[nt] : sv[nt][2 * e];
-          const float x1 = first ? sv[nt][2 * e + 1] + neg_ref[nt] : sv[nt][2 * e + 1];
+          const float x0 = !kPreScaled ? __builtin_fmaf(sv[nt][2 * e], c2, neg_ref[nt])
+                           : first     ? sv[nt][2 * e] + neg_ref[nt]
+                                       : sv[nt][2 * e];
+          const float x1 = !kPreScaled ? __builtin_fmaf(sv[nt][2 * e + 1], c2, neg_ref[nt])
+                           : first     ? sv[nt][2 * e + 1] + neg_ref[nt]
+                                       : sv[nt][2 * e + 1];
           pb[nt][e] = pack_bf16(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
           l_part[nt] = sum_bf16x2(pb[nt][e], l_part[nt]);
         }
@@ -929,6 +940,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       // Q scaled by scale * log2(e) and rounded once more to bf16, so the
       // scores come out of the matrix cores in log2 units (no multiply per
       // score in the softmax)
+      if (kPreScaled)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -1065,6 +1077,7 @@ void attention_kernel(AttnArgs a) {
 // shares -- bandwidth-bound streams beside the other CUs' matrix-bound wide
 // tiles -- and then, like every other workgroup, the wide tiles of their
 // list; the lists are balanced and keep each kv head's tiles on one XCD.
+template <bool kPreScaled>
 __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(AttnArgs a) {
   static_assert(pkv::kWideWaves == 8, "rows of eight workgroups of eight wavefronts");
   const int j = blockIdx.x;
@@ -1088,7 +1101,7 @@ __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(A
   }
   const int i0 = sload(a.wg_list, j);
   const int i1 = sload(a.wg_list, j + 1);
-  if (i0 < i1) run_wide_list(a, i0, i1);
+  if (i0 < i1) run_wide_list<kPreScaled>(a, i0, i1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1287,8 +1300,13 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
       return PKV_EINVAL;
     a.wg_list = reinterpret_cast<const int32_t *>(w + plan->wg_off);
     a.num_wg = nwg;
-    hipLaunchKernelGGL(attention_mixed_kernel, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
-                       as_stream(stream), a);
+    // the pre-scaled form at or below the pages' scale 1/sqrt(head_dim)
+    if (scale <= 1.0001f / sqrtf((float)plan->head_dim))
+      hipLaunchKernelGGL(attention_mixed_kernel<true>, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
+                         as_stream(stream), a);
+    else
+      hipLaunchKernelGGL(attention_mixed_kernel<false>, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
+                         as_stream(stream), a);
   } else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();

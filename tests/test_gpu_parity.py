@@ -246,6 +246,19 @@ def test_wide_lists_with_interior_chunks(dev, opts):
     check_attention(out, oracle.packed_attention(b), f"wide lists {opts}")
 
 
+@pytest.mark.parametrize("scale", [0.01, 0.0883883, 0.3, 1.0])
+def test_softmax_scales(dev, scale):
+    """Scales other than 1/sqrt(128): up to that scale prefill tiles fold
+    scale * log2(e) into Q (one more bf16 rounding), above it they apply it
+    in fp32 like decode items; every case against the oracle at its scale."""
+    import dataclasses
+    b = wl.make_batch("scales", [(300, 70), (0, 130), (900, 1), (64, 1)], seed=37)
+    b = dataclasses.replace(b, scale=np.float32(scale))
+    note(f"softmax scale {scale}")
+    out, _, _, _ = run_step(b, dev)
+    check_attention(out, oracle.packed_attention(b), f"scale {scale}")
+
+
 def test_nan_in_unused_slots_does_not_leak(dev):
     """Slots past each sequence's end in its last block hold NaN bits."""
     b = wl.make_batch("nan-tail", [(20, 1), (0, 7), (37, 2)], seed=34, pool="materialize")
