@@ -215,7 +215,10 @@ int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
  * results (running max, sum, unnormalised output) into ws; every other row
  * writes out directly.  Accumulation is fp32; probabilities are rounded to
  * bf16 for the P.V product and the normaliser sums those rounded values;
- * out is rounded to bf16 (nearest even).  Block-table entries outside
+ * out is rounded to bf16 (nearest even).  When scale <= 1/sqrt(head_dim),
+ * prefill tiles multiply q by scale * log2(e) once and round it to bf16
+ * again before the products (one more rounding of q); above that scale
+ * they, like decode items, apply the scale in fp32.  Block-table entries outside
  * [0, num_blocks) read as zero keys/values.  Errors: PKV_EINVAL (null
  * pointers, plan mismatch), PKV_ERANGE (num_blocks x num_kv_heads above
  * 2^32), PKV_EWORKSPACE, PKV_EHIP.
