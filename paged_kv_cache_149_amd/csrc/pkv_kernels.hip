@@ -189,16 +189,34 @@ __global__ __launch_bounds__(256) void append_kernel(
                                  (sl & 15) * kKGroup + d0 % kKGroup) = x;
     }
   }
-  {  // V: lanes over rows
-    const int i = tid & 15, d0 = 8 * (tid >> 4);
-    const int64_t sl = srow[i];
-    if (t0 + i < T && sl >= 0) {
-      const u32x4 x = load16(v_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
-      uint16_t *dst = vc + ((sl >> 4) * Hkv + h) * TILE + (int64_t)d0 * pkv::kBlock + (sl & 15);
+  {  // V: the 16 rows through LDS, then written dimension-major: lanes over
+     // (row pair, dimension), pairs fastest, so a wavefront's stores cover
+     // 8 dimensions x 16 tokens -- 32 contiguous bytes per dimension when
+     // the rows fill a block in order; a pair of consecutive, 4-byte-aligned
+     // slots is one 4-byte store
+    __shared__ uint32_t vrow[kAppendRows][D / 2 + 1];  // +1: rows start in different banks
+    {
+      const int i = tid >> 4, d0 = 8 * (tid & 15);
+      if (t0 + i < T) {
+        const u32x4 x = load16(v_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[(2 * e) * pkv::kBlock] = (uint16_t)(x[e] & 0xFFFF);
-        dst[(2 * e + 1) * pkv::kBlock] = (uint16_t)(x[e] >> 16);
+        for (int e = 0; e < 4; ++e) vrow[i][d0 / 2 + e] = x[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kAppendRows * D / 2 / 256; ++k) {
+      const int u = tid + 256 * k, p = u & 7, d = u >> 3;
+      const int r0 = 2 * p, r1 = r0 + 1;
+      const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
+      const uint32_t w0 = vrow[r0][d >> 1], w1 = vrow[r1][d >> 1];
+      const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
+      if (s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0) {
+        *reinterpret_cast<uint32_t *>(vc + ((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)) =
+            a0 | (a1 << 16);
+      } else {
+        if (s0 >= 0) vc[((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)] = (uint16_t)a0;
+        if (s1 >= 0) vc[((s1 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s1 & 15)] = (uint16_t)a1;
       }
     }
   }
