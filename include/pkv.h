@@ -219,9 +219,12 @@ int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
  * prefill tiles multiply q by scale * log2(e) once and round it to bf16
  * again before the products (one more rounding of q); above that scale
  * they, like decode items, apply the scale in fp32.  Block-table entries outside
- * [0, num_blocks) read as zero keys/values.  Errors: PKV_EINVAL (null
- * pointers, plan mismatch), PKV_ERANGE (num_blocks x num_kv_heads above
- * 2^32), PKV_EWORKSPACE, PKV_EHIP.
+ * [0, num_blocks) read as zero keys/values.  scale must be positive and
+ * finite (the kernels take maxima of raw scores and scale them afterwards,
+ * which only a positive scale commutes with).  Errors: PKV_EINVAL (null
+ * pointers, plan mismatch, a scale that is not positive and finite -- checked
+ * before anything else), PKV_ERANGE (num_blocks x num_kv_heads above 2^32),
+ * PKV_EWORKSPACE, PKV_EHIP.
  * ------------------------------------------------------------------------- */
 int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                               const pkv_bf16 *v_cache,
@@ -253,7 +256,8 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
 /* ---------------------------------------------------------------------------
  * The whole step on one stream: pkv_slot_append (slot_mapping, device
  * int64[T], is written), then pkv_paged_varlen_attention.  Attention reads the cache
- * after the append, so each row sees its own new key.
+ * after the append, so each row sees its own new key.  A scale that is not
+ * positive and finite returns PKV_EINVAL before the append is launched.
  * ------------------------------------------------------------------------- */
 int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
                    const pkv_bf16 *v_new, pkv_bf16 *k_cache,
@@ -312,8 +316,9 @@ int pkv_qkv_rope(const pkv_bf16 *x, const pkv_bf16 *w_qkv, int32_t num_rows, int
  * y = attn w_o^T with pkv_linear.  w_o: device bf16[hidden][Hq * 128].
  * The caller provides q, k_new, v_new (as above) and attn bf16[T][Hq][128];
  * y: bf16[T][hidden].  The plan, workspace, pools and metadata are those of
- * pkv_paged_step.  hidden must be a multiple of 128 (PKV_EUNSUPPORTED
- * before anything is launched).  Errors: those of the three calls.
+ * pkv_paged_step.  hidden must be a multiple of 128 (PKV_EUNSUPPORTED) and
+ * scale positive and finite (PKV_EINVAL), both checked before anything is
+ * launched.  Errors: those of the three calls.
  * ------------------------------------------------------------------------- */
 int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *w_o, int32_t hidden,
                       pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q, const int32_t *seq_lens,

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include <algorithm>
+#include <cfloat>
 
 #include "pkv_internal.h"
 
@@ -1211,6 +1212,11 @@ inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP; }
 
+// The softmax scale must be a positive, finite number: the kernels take
+// maxima of raw scores and scale them afterwards, which only a positive
+// scale commutes with.
+inline bool valid_scale(float scale) { return scale > 0.f && scale <= FLT_MAX; }
+
 int check_plan(const pkv_plan_t *plan, size_t ws_bytes, const void *ws) {
   if (!plan) return PKV_EINVAL;
   if (plan->head_dim != D || plan->num_q_heads <= 0 || plan->num_kv_heads <= 0) return PKV_EINVAL;
@@ -1279,6 +1285,7 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                               pkv_stream_t stream) {
   int st = check_plan(plan, ws_bytes, ws);
   if (st != PKV_OK) return st;
+  if (!valid_scale(scale)) return PKV_EINVAL;
   if (plan->num_items == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !out || bt_stride <= 0 || num_blocks <= 0)
     return PKV_EINVAL;
@@ -1433,7 +1440,7 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
                    int64_t num_blocks, int64_t *slot_mapping, float scale,
                    const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream) {
-  if (!plan) return PKV_EINVAL;
+  if (!plan || !valid_scale(scale)) return PKV_EINVAL;
   const int st = pkv_slot_append(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride,
                                  plan->num_seqs, plan->num_rows, num_blocks, slot_mapping, k_cache,
                                  v_cache, plan->num_kv_heads, plan->head_dim, stream);

@@ -32,6 +32,7 @@
 // same lane, and the rotation needs no data exchange.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -483,7 +484,9 @@ int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *
                       float scale, float rope_theta, const pkv_plan_t *plan, void *ws, size_t ws_bytes,
                       pkv_bf16 *q, pkv_bf16 *k_new, pkv_bf16 *v_new, pkv_bf16 *attn, pkv_bf16 *y,
                       pkv_stream_t stream) {
-  if (!plan) return PKV_EINVAL;
+  // the scale is checked by pkv_paged_step too; here it is checked before
+  // the projection is launched
+  if (!plan || !(scale > 0.f && scale <= FLT_MAX)) return PKV_EINVAL;
   // the output projection's features are the hidden size: checked before
   // anything is launched
   if (hidden <= 0 || hidden % kHead != 0) return PKV_EUNSUPPORTED;

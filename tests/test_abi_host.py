@@ -228,3 +228,26 @@ def test_workspace_size_query_and_too_small(lib):
     assert st.host_bytes > 0 and st.ws_bytes > st.host_bytes and st.num_merge == 32
     buf = (ctypes.c_char * 16)()
     assert lib.pkv_plan(*args, ctypes.cast(buf, ctypes.c_void_p), 16, None, 0, ctypes.byref(st), None) == 4
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, float("nan"), float("inf"), -float("inf")])
+def test_entry_points_reject_a_scale_that_is_not_positive_and_finite(lib, scale):
+    """The scale is checked before anything is launched.  An empty step
+    (no rows, so no item) is used: with a valid scale every call below
+    returns PKV_OK without a launch, so no device pointer is ever used."""
+    st = binding.PlanStruct()
+    cu = np.zeros(1, dtype=np.int32)
+    args = [cu.ctypes.data_as(ctypes.c_void_p), None, 0, 0, 32, 8, 128, None, 0, 0, None]
+    buf = (ctypes.c_char * 65536)()
+    assert lib.pkv_plan(*args, ctypes.cast(buf, ctypes.c_void_p), 65536, None, 0, ctypes.byref(st), None) == 0
+    assert st.num_items == 0 and st.num_rows == 0 and st.ws_bytes <= 65536
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation returns first
+    ws = ctypes.cast(buf, ctypes.c_void_p)
+    f32 = ctypes.c_float
+    for good, want in ((0.0883883, 0), (scale, 1)):
+        assert lib.pkv_varlen_attention_main(fake, fake, fake, fake, 1, 64, f32(good), ctypes.byref(st), ws,
+                                             65536, fake, None) == want
+        assert lib.pkv_paged_varlen_attention(fake, fake, fake, fake, 1, 64, f32(good), ctypes.byref(st), ws,
+                                              65536, fake, None) == want
+        assert lib.pkv_paged_step(fake, fake, fake, fake, fake, fake, fake, fake, 1, 64, fake, f32(good),
+                                  ctypes.byref(st), ws, 65536, fake, None) == want
