@@ -255,48 +255,53 @@ def packed_attention_rows(batch, rows: Sequence[int]) -> Dict[int, np.ndarray]:
     return res
 
 
+def _packed_key_axis(cached_lens, q_lens):
+    """Sequence index and position of every key on one packed key axis that
+    holds all sequences' cached keys, then all new rows, each part in
+    sequence order; and the same two labels for the query rows (the new
+    rows).  Sequence s's cached keys sit at positions 0 .. c_s - 1 and its
+    new rows at c_s .. c_s + n_s - 1."""
+    c = np.asarray(cached_lens, dtype=np.int64)
+    n = np.asarray(q_lens, dtype=np.int64)
+    ids = np.arange(c.shape[0], dtype=np.int64)
+    # position inside a run = running index minus the index the run starts at
+    cached_pos = np.arange(int(c.sum())) - np.repeat(np.cumsum(c) - c, c)
+    row_pos = np.arange(int(n.sum())) - np.repeat(np.cumsum(n) - n, n) + np.repeat(c, n)
+    row_seq = np.repeat(ids, n)
+    key_seq = np.concatenate([np.repeat(ids, c), row_seq])
+    key_pos = np.concatenate([cached_pos, row_pos])
+    return key_seq, key_pos, row_seq, row_pos
+
+
+def _block_diagonal_causal(key_seq, key_pos, row_seq, row_pos) -> np.ndarray:
+    """[K4I] "防止跨请求 attention": row i may read key j exactly when both
+    belong to the same request and j's position is not after i's."""
+    return (row_seq[:, None] == key_seq[None, :]) & (key_pos[None, :] <= row_pos[:, None])
+
+
 def dense_mask_attention(batch, seqs: Sequence[int] | None = None) -> np.ndarray:
-    """Second, independent formulation ([MLM] "完整实现"): all sequences'
-    cached keys, then all new rows, laid out as ONE key axis; each key and
-    each query carries a (sequence, position) tag; a dense mask allows
-    (same sequence) and (key position <= query position); one softmax per
-    query row over the whole key axis.  Uses the corrected key layout
-    [cached | new] (the printed visualiser's form).  Returns [Tsel, Hq, D]
-    for the selected sequences' rows in packed order."""
+    """Second, independent formulation ([MLM] "完整实现"; mask rule of [K4I]
+    "防止跨请求 attention"): the selected sequences' cached keys, then their
+    new rows, laid out as ONE key axis with a (sequence, position) label per
+    key and per query; a dense block-diagonal causal mask over that axis;
+    one softmax per query row over the whole key axis.  Returns
+    [Tsel, Hq, D] for the selected sequences' rows in packed order."""
     st = step_from_batch(batch)
     cu, sl = st["cu"], st["seq_lens"]
-    S = sl.shape[0]
-    sel = list(range(S)) if seqs is None else list(seqs)
+    sel = np.arange(sl.shape[0]) if seqs is None else np.asarray(list(seqs), dtype=np.int64)
     Hq, D, Hkv = st["q"].shape[1], st["D"], st["H_kv"]
     G = Hq // Hkv
-    key_seq, key_pos, Ks, Vs = [], [], [], []
-    for s in sel:
-        q_len = int(cu[s + 1] - cu[s])
-        c = int(sl[s]) - q_len
-        Kc, Vc = gather_kv(batch.k_pool, batch.v_pool, st["bt"][s], c, Hkv, D)
-        key_seq += [s] * c
-        key_pos += list(range(c))
-        Ks.append(Kc)
-        Vs.append(Vc)
-    q_seq, q_pos, q_rows = [], [], []
-    for s in sel:
-        q_len = int(cu[s + 1] - cu[s])
-        c = int(sl[s]) - q_len
-        for j in range(q_len):
-            q_seq.append(s)
-            q_pos.append(c + j)
-            q_rows.append(int(cu[s]) + j)
-    key_seq += q_seq
-    key_pos += q_pos
-    Ks.append(st["k_new"][q_rows])
-    Vs.append(st["v_new"][q_rows])
-    K = np.concatenate(Ks, axis=0)
-    V = np.concatenate(Vs, axis=0)
-    allowed = (np.array(q_seq)[:, None] == np.array(key_seq)[None, :]) & \
-              (np.array(key_pos)[None, :] <= np.array(q_pos)[:, None])
-    mask = np.where(allowed, 0.0, -np.inf)
+    q_lens = cu[sel + 1] - cu[sel]
+    cached = sl[sel] - q_lens
+    key_seq, key_pos, row_seq, row_pos = _packed_key_axis(cached, q_lens)
+    # packed row index of every selected query row
+    q_rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in sel]) if len(sel) else np.zeros(0, np.int64)
+    gathered = [gather_kv(batch.k_pool, batch.v_pool, st["bt"][s], int(c), Hkv, D) for s, c in zip(sel, cached)]
+    K = np.concatenate([kv[0] for kv in gathered] + [st["k_new"][q_rows]], axis=0)
+    V = np.concatenate([kv[1] for kv in gathered] + [st["v_new"][q_rows]], axis=0)
+    mask = np.where(_block_diagonal_causal(key_seq, key_pos, row_seq, row_pos), 0.0, -np.inf)
     Q = st["q"][q_rows]
-    out = np.empty((len(q_rows), Hq, D), dtype=np.float64)
+    out = np.empty((q_rows.shape[0], Hq, D), dtype=np.float64)
     for h in range(Hq):
         scores = (Q[:, h, :] @ K[:, h // G, :].T) * st["scale"] + mask
         m = scores.max(axis=1, keepdims=True)
@@ -311,18 +316,7 @@ def visibility_grid(kv_lens: Sequence[int], q_lens: Sequence[int]) -> np.ndarray
     for sequences with ``kv_lens`` cached and ``q_lens`` new tokens: key axis
     [all cached | all new], allowed iff same sequence and key position <=
     query position."""
-    key_seq, key_pos, q_seq, q_pos = [], [], [], []
-    for s, c in enumerate(kv_lens):
-        key_seq += [s] * c
-        key_pos += list(range(c))
-    for s, (c, n) in enumerate(zip(kv_lens, q_lens)):
-        for j in range(n):
-            q_seq.append(s)
-            q_pos.append(c + j)
-    key_seq += q_seq
-    key_pos += q_pos
-    return (np.array(q_seq)[:, None] == np.array(key_seq)[None, :]) & \
-           (np.array(key_pos)[None, :] <= np.array(q_pos)[:, None])
+    return _block_diagonal_causal(*_packed_key_axis(kv_lens, q_lens))
 
 
 def score_shapes(cu_seqlens_q, seq_lens) -> List[Tuple[int, int]]:
