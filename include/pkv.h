@@ -335,7 +335,7 @@ int pkv_layer_forward(const pkv_bf16 *x, const pkv_bf16 *w_qkv, const pkv_bf16 *
  * Host block pool ("连续批处理与 PagedAttention 原理", section "块管理器": the
  * physical block pool records which blocks are free and a reference count
  * per block in use; its operations are allocate, free and copy-on-write.
- * "11.2 连续批处理与 PagedAttention", section 11.2.3 "共享": several logical
+ * "11.2 连续批处理与 PagedAttention", section 11.2.3 (sharing): several logical
  * blocks may map to one physical block; when the output sequences of one
  * request share the prompt's blocks, only a shared block that is not yet
  * full is copied before a sequence writes into it; shared full prefix

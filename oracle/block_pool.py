@@ -11,7 +11,7 @@ What the pages fix (cited per function):
   copy-on-write (when two sequences share a physical block and one of them
   must write a new token into it, the block is copied first and the other
   sequence is unaffected).
-* [YB] "11.2 连续批处理与 PagedAttention", section 11.2.3 "共享" and Figure
+* [YB] "11.2 连续批处理与 PagedAttention", section 11.2.3 (sharing) and Figure
   11-4: several logical blocks may map to one physical block; within one
   request, parallel samples share all of the prompt's blocks and only the
   last, not yet full block is copied when a sample writes into a block whose

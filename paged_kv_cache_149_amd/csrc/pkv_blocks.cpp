@@ -1,7 +1,7 @@
 // Host-side physical block pool of a paged KV cache: which blocks are free,
 // and a reference count for every block in use ("连续批处理与 PagedAttention
 // 原理", section "块管理器": allocate, free and copy-on-write; "11.2 连续批处理
-// 与 PagedAttention", section 11.2.3 "共享": several logical blocks may map to
+// 与 PagedAttention", section 11.2.3 (sharing): several logical blocks may map to
 // one physical block, and only a shared block that is not yet full is
 // copied before a sequence writes into it).
 //

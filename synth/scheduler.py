@@ -4,12 +4,13 @@ drives one packed attention step per iteration.
 Policy (from the pages; readings where they leave a choice):
 
 * Iteration-level scheduling: after every step finished requests leave and
-  waiting ones are admitted ([MLM] "动态调度"; [YB] 11.2.2, three things per
+  waiting ones are admitted ([MLM] "连续批处理：动态调度与不规则批处理"; [YB] 11.2.2, three things per
   step; [CB] "Scheduler 的三个数据结构").
 * A per-step token budget (max_num_batched_tokens): decode rows first, then
   requests still prefilling, then first-come-first-served admission of
-  waiting requests, each chunked into the budget left ([YB] 11.2.5
-  "先装下全部 Decode 词元，剩下的留给 Prefill 块"; [CB] chunked prefill).
+  waiting requests, each chunked into the budget left ([YB] 11.2.5:
+  the decode tokens are placed first and prefill chunks fill the rest;
+  [CB] chunked prefill).
   An optional cap on running sequences (max_num_seqs) bounds concurrency.
 * Paged blocks of 16 tokens from a fixed pool, allocated when a sequence
   needs a new block and all returned when it finishes ([PA] "分页设计";
@@ -21,7 +22,8 @@ Policy (from the pages; readings where they leave a choice):
   scheduled, ties to the most recently admitted ([CB] "Preemption 优先级":
   LRU).
 * A step that finishes a request's known tokens samples one token
-  ([K4I] "prefill 结束时也会产生第一个输出 token"); a request is done when it
+  ([K4I], section "与 KV cache 的关系": the step that completes a prefill
+  also yields the first output token); a request is done when it
   has generated its output length (EOS at the drawn length).
 
 A request's tokens are its prompt followed by what it generated; ``computed``
