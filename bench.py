@@ -1,22 +1,24 @@
 #!/usr/bin/env python3
-"""Throughput of one packed, ragged attention step over a paged KV cache on
+"""Throughput of the packed, ragged attention step over a paged KV cache on
 one MI355X.
 
-A step is the whole hot path on one synthetic batch resident in HBM: slot
-translation + KV append (one launch), the fused attention launch and the
-split merge -- the calls pkv_paged_step makes, issued one by one so the
-attention launch can be bracketed with HIP events on its stream.  The default
-workload is the decode-only step: 64 sequences, one query row each,
-cached contexts uniform in [128, 4096], 32 query / 8 KV heads, head_dim 128,
-bf16.
+The default workload is the continuous-batching trace: a seeded
+iteration-level scheduler's 200 iterations (8192-token budget, chunked
+prefill, recompute preemption, 65,536-block pool), each running the whole
+hot path -- slot translation + KV append (one launch), the fused attention
+launch, the split merge -- for each of 32 layers (32 query / 8 KV heads,
+head_dim 128, bf16).  One bench step is one pass over the whole trace; HIP
+events on the library's stream bracket every iteration and every attention
+launch.
 
-Before every timed step a 1 GiB read evicts L2 and the Infinity Cache, so
-no step finds the previous one's KV on chip; step time and the attention
-launch are taken with HIP events on the library's stream, flush excluded.
+The single-step workloads (--workload decode64, mixed, longshared, ...)
+time K steps of one batch resident in HBM; before each, a 1 GiB read evicts
+L2 and the Infinity Cache, so no step finds the previous one's KV on chip.
 
 Prints ONE JSON line.  `value` is KV GB/s over the whole step (unique KV
 bytes / step time); query tok/s, the attention kernel's roofline fraction
-and the fp64 CPU oracle's rate on the same batch are reported beside it.
+and the fp64 CPU oracle's rate on a sample of the same workload are
+reported beside it.
 """
 
 from __future__ import annotations
@@ -49,9 +51,10 @@ WORKLOADS = {
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode64", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap", "prefixcache", "layer"])
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (trace: passes over the whole trace; default 5, else 50)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps first (trace: default 1, else 5)")
+    p.add_argument("--workload", default="trace", choices=sorted(WORKLOADS) + ["trace", "blockcopy", "swap", "prefixcache", "layer"])
     p.add_argument("--trace-steps", type=int, default=200, help="trace workload: scheduler steps")
     p.add_argument("--layer-batch", default="mixed", choices=sorted(WORKLOADS),
                    help="layer workload: the step whose rows the layer runs on")
@@ -69,7 +72,12 @@ def parse():
                    help="only measure plain streaming read and copy rates with torch kernels")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB fp32 copy kernel 5 times (HBM counter calibration)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.steps is None:
+        args.steps = 5 if args.workload == "trace" else 50
+    if args.warmup is None:
+        args.warmup = 1 if args.workload == "trace" else 5
+    return args
 
 
 def copy_calibration():
@@ -279,11 +287,19 @@ def main():
 
 
 def run_trace(args):
-    """The continuous-batching trace: the seeded scheduler's steps, each one
-    packed step (pkv_paged_step: slot translation + append, attention,
-    merge) for every layer, each layer with its own 65,536-block K and V
-    caches.  Each step's per-layer Q/K/V are N(0,1) drawn on the device
-    before its timed region; HIP events bracket the step's layer loop."""
+    """The continuous-batching trace: the seeded scheduler's 200 iterations
+    (Poisson(8) arrivals, prompts U{32..2048}, outputs log-uniform in
+    [10, 2000], 8192-token budget with chunked prefill, recompute
+    preemption, 65,536-block pool), each one packed step for every one of
+    the 32 layers -- slot translation + append, the attention launch, the
+    split merge -- each layer with its own K and V pools.
+
+    One bench step is one pass over the whole trace.  Per iteration, every
+    layer's Q/K/V rows are N(0,1) drawn on the device before the
+    iteration's first event, and the iteration is planned on the host
+    (pkv_plan into one of two pinned staging buffers) while the device still
+    runs the previous ones.  HIP events on the stream bracket each
+    iteration's layer loop and every attention launch."""
     import torch
     import paged_kv_cache_149_amd as pkv
     from paged_kv_cache_149_amd import accounting
@@ -292,10 +308,13 @@ def run_trace(args):
     dev = torch.device("cuda", 0)
     pkv.load_library()
     cfg = sc.TraceConfig(steps=args.trace_steps)
+    t0 = time.perf_counter()
     steps, sch = sc.continuous_batching_trace(cfg)
+    sched_s = time.perf_counter() - t0
     L, Hq, Hkv, D, NB = args.layers, 32, 8, 128, cfg.num_blocks
-    log(f"trace: {len(steps)} steps, {L} layers, {NB}-block pool per layer, "
-        f"{sch.preemptions} preemptions, {len(sch.finished)} requests finished")
+    n_it = len(steps)
+    log(f"trace: {n_it} iterations, {L} layers, {NB}-block pool per layer, "
+        f"{sch.preemptions} preemptions, {len(sch.finished)} requests finished (scheduler {sched_s:.2f} s)")
     kc = [torch.empty(NB, Hkv, 16, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
     vc = [torch.empty(NB, Hkv, D, 16, dtype=torch.bfloat16, device=dev) for _ in range(L)]
     Tmax = max(st.num_rows for st in steps)
@@ -308,73 +327,216 @@ def run_trace(args):
     gen.manual_seed(cfg.seed)
     stream = torch.cuda.current_stream(dev)
     scale = 1.0 / (D ** 0.5)
-    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    plans, events, recs = [], [], []
+
+    # device metadata of every iteration, uploaded once; algorithmic work
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    meta = [(i32(st.cu_seqlens_q), i32(st.seq_lens), i32(st.block_tables)) for st in steps]
+    att_bytes = np.zeros(n_it)
+    app_bytes = np.zeros(n_it)
+    kv_unique = np.zeros(n_it)
+    flop = np.zeros(n_it)
     for i, st in enumerate(steps):
-        T = st.num_rows
-        qa[:, :T].normal_(generator=gen)
-        ka[:, :T].normal_(generator=gen)
-        va[:, :T].normal_(generator=gen)
-        plan = pkv.pkv_plan(st.cu_seqlens_q, st.seq_lens, Hq, Hkv, D, block_tables=st.block_tables,
-                            num_blocks=NB, device=dev, workspace=ws, stream=stream)
-        ws = plan.workspace
-        cu = torch.from_numpy(st.cu_seqlens_q).to(dev)
-        sl = torch.from_numpy(st.seq_lens).to(dev)
-        bt = torch.from_numpy(np.ascontiguousarray(st.block_tables)).to(dev)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for l in range(L):
-            pkv.pkv_paged_step(qa[l, :T], ka[l, :T], va[l, :T], kc[l], vc[l], cu, sl, bt, scale, plan,
-                               slot_mapping=slots[:T], out=out[:T], stream=stream)
-        b.record(stream)
-        plans.append(plan)
-        events.append((a, b))
-        nbytes = accounting.step_bytes(st.cu_seqlens_q, st.seq_lens, st.block_tables, Hq, Hkv, D)
-        flop = accounting.attention_flop(st.cu_seqlens_q, st.seq_lens, Hq, D)
-        recs.append((T, st.n_decode, nbytes["total"] + nbytes["append"], nbytes["kv_unique"], flop))
-        if i % 50 == 0:
-            log(f"step {i}: {T} rows ({st.n_decode} decode), {len(st.rows)} sequences")
-    torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in events])
-    rows = np.array([r[0] for r in recs])
-    byts = np.array([r[2] for r in recs], dtype=np.float64) * L
-    kvb = np.array([r[3] for r in recs], dtype=np.float64) * L
-    flop = np.array([r[4] for r in recs], dtype=np.float64) * L
-    t_hbm = byts / (HBM_PEAK_GBS * 1e9)
-    t_mfma = flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
-    sec = ms * 1e-3
+        nb_ = accounting.step_bytes(st.cu_seqlens_q, st.seq_lens, st.block_tables, Hq, Hkv, D)
+        att_bytes[i], app_bytes[i], kv_unique[i] = nb_["total"], nb_["append"], nb_["kv_unique"]
+        flop[i] = accounting.attention_flop(st.cu_seqlens_q, st.seq_lens, Hq, D)
+    rows = np.array([st.num_rows for st in steps], dtype=np.float64)
+
+    ws = [torch.empty(32 << 20, dtype=torch.uint8, device=dev)]
+    staging = [torch.empty(4 << 20, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    pending = [None, None]  # the plan whose copy last read each staging buffer
+    new_ev = lambda: torch.cuda.Event(enable_timing=True)
+    ev_it = [(new_ev(), new_ev()) for _ in range(n_it)]
+    ev_at = [[(new_ev(), new_ev()) for _ in range(L)] for _ in range(n_it)]
+    kernels = set()
+
+    def one_pass():
+        plan_us = np.zeros(n_it)
+        for i, st in enumerate(steps):
+            T = st.num_rows
+            qa[:, :T].normal_(generator=gen)
+            ka[:, :T].normal_(generator=gen)
+            va[:, :T].normal_(generator=gen)
+            k = i % 2
+            if pending[k] is not None:
+                pending[k].event.synchronize()
+            plan = pkv.pkv_plan(st.cu_seqlens_q, st.seq_lens, Hq, Hkv, D, block_tables=st.block_tables,
+                                num_blocks=NB, device=dev, workspace=ws[0], staging=staging[k], stream=stream)
+            pending[k] = plan
+            ws[0] = plan.workspace
+            plan_us[i] = plan.host_us
+            kernels.add("attention_mixed_kernel" if plan.num_wide_items > 0 else "attention_kernel")
+            cu, sl, bt = meta[i]
+            ev_it[i][0].record(stream)
+            for l in range(L):
+                pkv.pkv_slot_append(ka[l, :T], va[l, :T], cu, sl, bt, kc[l], vc[l], slot_mapping=slots[:T],
+                                    stream=stream)
+                ev_at[i][l][0].record(stream)
+                pkv.pkv_varlen_attention_main(qa[l, :T], kc[l], vc[l], bt, scale, plan, out=out[:T], stream=stream)
+                ev_at[i][l][1].record(stream)
+                pkv.pkv_split_kv_reduce(plan, out[:T], stream=stream)
+            ev_it[i][1].record(stream)
+        torch.cuda.synchronize()
+        it_ms = np.array([a.elapsed_time(b) for a, b in ev_it])
+        at_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev_at])
+        return it_ms, at_ms, plan_us
+
+    for w in range(args.warmup):
+        one_pass()
+        log(f"warmup pass {w + 1}/{args.warmup} done")
+    it_all, at_all, plan_all = [], [], []
+    for p in range(args.steps):
+        it_ms, at_ms, plan_us = one_pass()
+        it_all.append(it_ms)
+        at_all.append(at_ms)
+        plan_all.append(plan_us)
+        log(f"pass {p + 1}/{args.steps}: {it_ms.sum():.1f} ms over {n_it} iterations "
+            f"(attention launches {at_ms.sum():.1f} ms)")
+    it_all = np.array(it_all)            # [pass, iteration]
+    at_all = np.array(at_all)            # [pass, iteration, layer]
+    plan_all = np.array(plan_all)
+
+    sec_it = it_all.mean(axis=0) * 1e-3                  # per iteration, all layers
+    pass_ms = it_all.sum(axis=1)
+    t_hbm = (att_bytes + app_bytes) * L / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flop * L / (BF16_MFMA_PEAK_TFLOPS * 1e12)
     dec = t_hbm >= t_mfma
     pre = ~dec
+    # the attention launches alone: per-launch algorithmic bytes / FLOP over
+    # their event-timed durations
+    at_sec = at_all * 1e-3
+    n_launch = at_all.size
+    la_bytes = np.broadcast_to(att_bytes[None, :, None], at_all.shape)
+    la_flop = np.broadcast_to(flop[None, :, None], at_all.shape)
+    l_hbm = la_bytes / (HBM_PEAK_GBS * 1e9)
+    l_mfma = la_flop / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    l_dec = l_hbm >= l_mfma
+    achieved = la_bytes.sum() / at_sec.sum() / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("trace", f"cb-trace-{n_it}steps-{L}layers"),
+            "kernel": "+".join(sorted(kernels)), "launches": int(n_launch),
+            "avg_ms": round(float(at_all.mean()), 5), "bytes_per_launch": round(float(la_bytes.mean()), 1),
+            "flop_per_launch": round(float(la_flop.mean()), 1),
+            "frac_per_launch_bound": round(float(np.maximum(l_hbm, l_mfma).sum() / at_sec.sum()), 4),
+            "decode_heavy_launches": {"n": int(l_dec.sum()),
+                                      "hbm_frac": round(float(la_bytes[l_dec].sum() / at_sec[l_dec].sum()
+                                                              / (HBM_PEAK_GBS * 1e9)), 4) if l_dec.any() else None},
+            "prefill_heavy_launches": {"n": int((~l_dec).sum()),
+                                       "mfma_frac": round(float(la_flop[~l_dec].sum() / at_sec[~l_dec].sum()
+                                                                / (BF16_MFMA_PEAK_TFLOPS * 1e12)), 4)
+                                       if (~l_dec).any() else None}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = trace_cpu_baseline(steps, cfg, kv_unique, L, dev)
     res = {
         "metric": METRIC,
-        "value": round(kvb.sum() / sec.sum() / 1e9, 2),
+        "value": round(kv_unique.sum() * L / sec_it.sum() / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": len(steps),
-        "warmup": 0,
-        "ms_per_step": round(float(ms.mean()), 4),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(pass_ms.mean()), 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"cb-trace-{len(steps)}steps-{L}layers", "layers": L, "budget": cfg.token_budget,
-                   "pool_blocks": NB, "arrival_rate": cfg.arrival_rate, "preemptions": sch.preemptions,
-                   "finished": len(sch.finished)},
-        "query_tok_s": round(rows.sum() / sec.sum(), 1),
+        "config": {"workload": f"cb-trace-{n_it}steps-{L}layers", "step": "one pass over the whole trace",
+                   "iterations": n_it, "layers": L, "budget": cfg.token_budget, "pool_blocks": NB,
+                   "arrival_rate": cfg.arrival_rate, "preemptions": sch.preemptions,
+                   "finished": len(sch.finished), "q_heads": Hq, "kv_heads": Hkv, "head_dim": D},
+        "query_tok_s": round(rows.sum() / sec_it.sum(), 1),
         "total_rows": int(rows.sum()),
-        "total_ms": round(float(ms.sum()), 3),
-        "roofline_fraction": round(float(np.maximum(t_hbm, t_mfma).sum() / sec.sum()), 4),
+        "ms_per_iteration": round(float(sec_it.mean() * 1e3), 4),
+        "pass_ms_min_max": [round(float(pass_ms.min()), 3), round(float(pass_ms.max()), 3)],
+        "roofline_fraction": round(float(np.maximum(t_hbm, t_mfma).sum() / sec_it.sum()), 4),
         "decode_heavy": {"steps": int(dec.sum()),
-                         "hbm_frac": round(float(byts[dec].sum() / sec[dec].sum() / (HBM_PEAK_GBS * 1e9)), 4)
-                         if dec.any() else None},
+                         "hbm_frac": round(float((att_bytes + app_bytes)[dec].sum() * L / sec_it[dec].sum()
+                                                 / (HBM_PEAK_GBS * 1e9)), 4) if dec.any() else None},
         "prefill_heavy": {"steps": int(pre.sum()),
-                          "mfma_frac": round(float(flop[pre].sum() / sec[pre].sum() / (BF16_MFMA_PEAK_TFLOPS * 1e12)), 4)
-                          if pre.any() else None,
-                          "ms": round(float(ms[pre].sum()), 3) if pre.any() else None},
-        "per_step_ms_first": [round(float(x), 3) for x in ms[:8]],
+                          "mfma_frac": round(float(flop[pre].sum() * L / sec_it[pre].sum()
+                                                   / (BF16_MFMA_PEAK_TFLOPS * 1e12)), 4) if pre.any() else None,
+                          "ms": round(float(sec_it[pre].sum() * 1e3), 3) if pre.any() else None},
+        "host_plan_us": {"mean": round(float(plan_all.mean()), 1), "max": round(float(plan_all.max()), 1),
+                         "overlapped": "each iteration is planned while the device runs earlier ones"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def trace_cpu_baseline(steps, cfg, kv_unique, L, dev):
+    """The fp64 oracle, untuned, on a bounded sample of the trace: every
+    fourth sequence (packed order) of iterations n/8, n/2 and 7n/8 (25, 100
+    and 175 of 200) with the host's BLAS threads, and every sixteenth
+    sequence of iteration n/2 with one thread.  Values are the seeded counter generator's (pool tiles
+    generated on the device by the generator's torch form, then copied to
+    the host before timing).  The whole trace's oracle time is extrapolated
+    from the sampled rate by KV bytes, and labelled so."""
+    import dataclasses
+    import torch
+    import oracle
+    from synth import workloads as wl
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits, threads = None, cores
+    per_tok = 2 * 8 * 128 * 2
+
+    def sampled(index, every):
+        st = steps[index]
+        b = wl.batch_from_metadata(f"trace-{index}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
+                                   cfg.num_blocks, seed=cfg.seed + 100 * index)
+        sel = list(range(0, b.num_seqs, every))
+        used = np.unique(np.concatenate([b.block_tables[s, :(int(b.seq_lens[s]) + 15) // 16] for s in sel]))
+        idx = torch.from_numpy(used.astype(np.int64)).to(dev)
+        pools = []
+        for p in (b.k_pool, b.v_pool):
+            tiles = p.to_device(dev)[idx].cpu().numpy().view(np.uint16)
+            pools.append(_Dense({int(x): tiles[j] for j, x in enumerate(used)}, p.shape))
+        b = dataclasses.replace(b, k_pool=pools[0], v_pool=pools[1])
+        torch.cuda.empty_cache()
+        nbytes = int(sum(int(b.seq_lens[s]) for s in sel)) * per_tok
+        nrows = int(sum(int(b.cu_seqlens_q[s + 1] - b.cu_seqlens_q[s]) for s in sel))
+        return b, sel, nbytes, nrows
+
+    n = len(steps)
+    picks = sorted({n // 8, n // 2, (7 * n) // 8})
+    log(f"cpu baseline: oracle on every 4th sequence of trace iterations {picks}")
+    tot_s, tot_b, tot_r = 0.0, 0, 0
+    for index in picks:
+        b, sel, nbytes, nrows = sampled(index, 4)
+        t0 = time.perf_counter()
+        oracle.packed_attention(b, sel)
+        dt = time.perf_counter() - t0
+        log(f"cpu baseline: iteration {index}: {len(sel)} sequences, {nbytes / 1e9:.3f} GB, {dt:.2f} s")
+        tot_s, tot_b, tot_r = tot_s + dt, tot_b + nbytes, tot_r + nrows
+    one = None
+    if threadpool_limits is not None:
+        b, sel, nbytes, nrows = sampled(n // 2, 16)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.packed_attention(b, sel)
+            dt = time.perf_counter() - t0
+        one = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "sample": f"every 16th sequence of iteration {n // 2} ({len(sel)} sequences, {nbytes / 1e9:.3f} GB "
+                         f"of KV), {dt:.2f} s with one BLAS thread"}
+        log(f"cpu baseline: one thread: {one['value']} GB/s")
+    rate = tot_b / tot_s
+    total_bytes = float(kv_unique.sum()) * L
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"every 4th sequence of trace iterations {picks}, one layer each "
+                      f"({tot_b / 1e9:.3f} GB of KV, {tot_r} query rows, {tot_s:.2f} s; fp64 numpy, "
+                      f"{threads} BLAS threads, host cores available: {cores})",
+            "query_tok_s": round(tot_r / tot_s, 2),
+            "extrapolated_trace_s": round(total_bytes / rate, 1),
+            "extrapolated": "whole trace (all iterations, all layers) at the sampled rate, by KV bytes",
+            "one_thread": one}
 
 
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction

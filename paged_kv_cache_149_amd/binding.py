@@ -13,6 +13,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import time
 from typing import Optional
 
 import numpy as np
@@ -236,6 +237,7 @@ class Plan:
         self.workspace = workspace
         self.staging = staging
         self.event = event
+        self.host_us = 0.0
 
     def __getattr__(self, k):
         return getattr(self.st, k)
@@ -267,9 +269,14 @@ class Plan:
 def pkv_plan(cu_seqlens_q: np.ndarray, seq_lens: np.ndarray, num_q_heads: int, num_kv_heads: int,
              head_dim: int = HEAD_DIM, block_tables: Optional[np.ndarray] = None,
              num_blocks: int = 0, options: Optional[dict] = None, device=None,
-             workspace: Optional[torch.Tensor] = None, stream=None, host_only: bool = False) -> Plan:
+             workspace: Optional[torch.Tensor] = None, stream=None, host_only: bool = False,
+             staging: Optional[torch.Tensor] = None) -> Plan:
     """Build the work plan from HOST copies of the metadata.  With
-    host_only=True nothing touches a GPU (the plan stays in host memory)."""
+    host_only=True nothing touches a GPU (the plan stays in host memory).
+    ``staging`` (a pinned uint8 tensor) is used instead of a new pinned
+    buffer when it is large enough; the caller must not reuse it until the
+    plan's ``event`` has completed.  ``plan.host_us`` is the time the
+    planning call itself took on the host."""
     lib = load_library()
     cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
@@ -293,17 +300,22 @@ def pkv_plan(cu_seqlens_q: np.ndarray, seq_lens: np.ndarray, num_q_heads: int, n
     dev = torch.device(device if device is not None else "cuda")
     if dev.index is None:
         dev = torch.device("cuda", torch.cuda.current_device())
-    staging = torch.empty(host_bytes, dtype=torch.uint8, pin_memory=True)
+    if staging is None or staging.numel() < host_bytes or not staging.is_pinned():
+        staging = torch.empty(host_bytes, dtype=torch.uint8, pin_memory=True)
     need = max(int(st.ws_bytes), 256)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    _check("pkv_plan", lib.pkv_plan(*args, _P(staging.data_ptr()), host_bytes,
-                                     _P(workspace.data_ptr()), workspace.numel(),
-                                     ctypes.byref(st), ctypes.c_void_p(s.cuda_stream)))
+    t0 = time.perf_counter()
+    rc = lib.pkv_plan(*args, _P(staging.data_ptr()), staging.numel(), _P(workspace.data_ptr()),
+                      workspace.numel(), ctypes.byref(st), ctypes.c_void_p(s.cuda_stream))
+    host_us = (time.perf_counter() - t0) * 1e6
+    _check("pkv_plan", rc)
     ev = torch.cuda.Event()
     ev.record(s)
-    return Plan(st, workspace, staging, ev)
+    plan = Plan(st, workspace, staging, ev)
+    plan.host_us = host_us
+    return plan
 
 
 def _attn_args(q, k_cache, v_cache, block_tables, plan: Plan, out):

@@ -614,19 +614,17 @@ __device__ __forceinline__ WideTile wide_tile(const AttnArgs &a, int idx) {
 }
 
 // A column's probabilities (relative to its reference) may sum to this
-// much: every one of them, and every output accumulator, then stays finite
-// in fp32 (|v| < 2^27).  A wavefront with a column sum past it, or not
-// finite, recomputes its columns.
+// much: every one of them then stays finite in fp32.  The output
+// accumulators sum probability x value and can still overflow when values
+// are large (beyond ~2^27 at this bound), so they are checked as well: a
+// wavefront with a column sum past the bound, or any sum or accumulator
+// that is not finite, recomputes its columns.
 constexpr float kRedoSum = 0x1p100f;
 
-// The wide tiles items[i0, i1) of one persistent workgroup.
-// kPreScaled: Q is multiplied by scale * log2(e) once per tile and rounded
-// to bf16 again, the S^T accumulators start at -(reference), and the
-// softmax needs no multiply per score.  The extra rounding perturbs each
-// log2-domain score by ~2^-9 relative per Q element, so the launch uses this
-// form only at or below the softmax scale 1/sqrt(head_dim); larger scales
-// take the exact form (the scale applied in fp32 in each exponent's FMA).
-template <bool kPreScaled>
+// The wide tiles items[i0, i1) of one persistent workgroup.  Scores leave
+// the matrix cores unscaled; each exponential's argument is one fp32 FMA,
+// score * (scale * log2(e)) - reference, so Q enters the products exactly
+// as stored, whatever the size of the logits.
 __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1) {
   constexpr int WV = pkv::kWideWaves;
   constexpr int NT = pkv::kWideCols / (16 * WV);  // MFMA column tiles per wavefront
@@ -832,13 +830,8 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         wait_lds_for(kop);
       }
       if (do_qk) {
-        // past the first chunk the accumulators start at -(reference), so
-        // the scores come out of the matrix cores ready for the exponential
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float r0 = kPreScaled && (kInterior || c >= 1) ? neg_ref[nt] : 0.f;
-          sc[nt][0] = sc[nt][1] = f32x4{r0, r0, r0, r0};
-        }
+        for (int nt = 0; nt < NT; ++nt) sc[nt][0] = sc[nt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -903,22 +896,16 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
           const float m = max3(max3(sv[nt][0], sv[nt][1], sv[nt][2]), max3(sv[nt][3], sv[nt][4], sv[nt][5]),
                                __builtin_fmaxf(sv[nt][6], sv[nt][7]));
           const float mx = xmax32(xmax16(m));
-          neg_ref[nt] = mx == neg_inf() ? 0.f : (kPreScaled ? -mx : -mx * c2);
+          neg_ref[nt] = mx == neg_inf() ? 0.f : -mx * c2;
         }
       }
-      // scores are in log2 units (Q pre-scaled); the first chunk's still
-      // lack the reference
-      const bool first = !kInterior && c == 0;
+      // exponent (log2 units) relative to the reference
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = !kPreScaled ? __builtin_fmaf(sv[nt][2 * e], c2, neg_ref[nt])
-                           : first     ? sv[nt][2 * e] + neg_ref[nt]
-                                       : sv[nt][2 * e];
-          const float x1 = !kPreScaled ? __builtin_fmaf(sv[nt][2 * e + 1], c2, neg_ref[nt])
-                           : first     ? sv[nt][2 * e + 1] + neg_ref[nt]
-                                       : sv[nt][2 * e + 1];
+          const float x0 = __builtin_fmaf(sv[nt][2 * e], c2, neg_ref[nt]);
+          const float x1 = __builtin_fmaf(sv[nt][2 * e + 1], c2, neg_ref[nt]);
           pb[nt][e] = pack_bf16(__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1));
           l_part[nt] = sum_bf16x2(pb[nt][e], l_part[nt]);
         }
@@ -956,17 +943,6 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         default: wait_vmcnt<7 * kLoadsPerIssue>(); break;
       }
       q_ready(qb);
-      // Q scaled by scale * log2(e) and rounded once more to bf16, so the
-      // scores come out of the matrix cores in log2 units (no multiply per
-      // score in the softmax)
-      if (kPreScaled)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            qb[nt][c][e] = pack_bf16(bf16_lo(qb[nt][c][e]) * c2, bf16_hi(qb[nt][c][e]) * c2);
     };
     constexpr std::integral_constant<int, 0> kAny{};
     constexpr std::integral_constant<int, 1> kSteadyStep{};
@@ -1018,11 +994,21 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) l_tot[nt] = xsum32(xsum16(l_part[nt]));
 
-    // did a column outgrow its reference?  (rare: recomputed after the list)
+    // did a column outgrow its reference, or an output accumulator
+    // overflow?  (rare: recomputed after the list.)  0 * x is 0 for every
+    // finite x and NaN otherwise, so one FMA per accumulator tests them all
+    // with nothing to overflow.
     {
       bool grew = false;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) grew |= !(l_tot[nt] <= kRedoSum);
+      for (int nt = 0; nt < NT; ++nt) {
+        float z = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z = __builtin_fmaf(acc[nt][dt][e], 0.f, z);
+        grew |= !(l_tot[nt] <= kRedoSum) || z != 0.f;
+      }
       if (__builtin_amdgcn_ballot_w64(grew)) {
         if (i - i0 < 64) redo |= 1ull << (i - i0);
         else redo_all = true;
@@ -1096,7 +1082,6 @@ void attention_kernel(AttnArgs a) {
 // shares -- bandwidth-bound streams beside the other CUs' matrix-bound wide
 // tiles -- and then, like every other workgroup, the wide tiles of their
 // list; the lists are balanced and keep each kv head's tiles on one XCD.
-template <bool kPreScaled>
 __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(AttnArgs a) {
   static_assert(pkv::kWideWaves == 8, "rows of eight workgroups of eight wavefronts");
   const int j = blockIdx.x;
@@ -1120,7 +1105,7 @@ __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(A
   }
   const int i0 = sload(a.wg_list, j);
   const int i1 = sload(a.wg_list, j + 1);
-  if (i0 < i1) run_wide_list<kPreScaled>(a, i0, i1);
+  if (i0 < i1) run_wide_list(a, i0, i1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1325,13 +1310,8 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
       return PKV_EINVAL;
     a.wg_list = reinterpret_cast<const int32_t *>(w + plan->wg_off);
     a.num_wg = nwg;
-    // the pre-scaled form at or below the pages' scale 1/sqrt(head_dim)
-    if (scale <= 1.0001f / sqrtf((float)plan->head_dim))
-      hipLaunchKernelGGL(attention_mixed_kernel<true>, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
-                         as_stream(stream), a);
-    else
-      hipLaunchKernelGGL(attention_mixed_kernel<false>, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
-                         as_stream(stream), a);
+    hipLaunchKernelGGL(attention_mixed_kernel, dim3((unsigned)nwg), dim3(64 * pkv::kWideWaves), 0,
+                       as_stream(stream), a);
   } else if (plan->num_waves > 0)
     hipLaunchKernelGGL(attention_kernel, dim3(plan->num_waves), dim3(64), 0, as_stream(stream), a);
   return launch_status();

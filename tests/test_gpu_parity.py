@@ -2,10 +2,11 @@
 
 Slot translation and append: bit-exact.  Attention: max-abs <= 2e-2 and
 mean-abs <= 2e-3 against the fp64 oracle over every compared element.
-Small configurations are compared whole; full-size ones on sampled rows,
-in the launch configuration the bench times (default plan options).
+Every config is compared whole (every element); only the 32K-prefix chunk,
+a diagnostic workload, is sampled.  Default plan options, as the bench runs.
 """
 
+import dataclasses
 import math
 import sys
 
@@ -110,28 +111,58 @@ def test_decode64_full(dev):
     check_attention(out, oracle.packed_attention(b), "decode64")
 
 
-def test_mixed_chunked_sampled_rows(dev):
-    b = wl.config_mixed_chunked()
-    note("mixed chunked-prefill step: 2048 rows (sampled)")
-    out, slots, t, plan = run_step(b, dev)
-    assert plan.num_wide_items > 0
-    check_append(b, slots, t)
-    rng = np.random.default_rng(5)
-    rows = sorted(set([0, 1, 255, 256, 511, 512, 700, 767, 768, 1000, 1023])
-                  | set(rng.integers(1024, 2048, size=48).tolist()))
-    ref = oracle.packed_attention_rows(b, rows)
-    check_attention(out[rows], np.stack([ref[r] for r in rows]), "mixed chunked (sampled)")
+def host_pools(batch, t):
+    """The batch with its pools replaced by host copies of what the seeded
+    generator wrote on the device (synth's torch form of the counter
+    generator, before any library call touched the pools), so the oracle
+    reads a whole multi-GB pool without generating it again on the CPU.
+    A sample of referenced tiles is checked against the numpy form of the
+    same generator first."""
+    nb, hkv = batch.num_blocks, batch.num_kv_heads
+    k = t["k_cache"].view(torch.int16).cpu().numpy().view(np.uint16).reshape(nb, hkv, -1)
+    v = t["v_cache"].view(torch.int16).cpu().numpy().view(np.uint16).reshape(nb, hkv, -1)
+    used = np.unique(batch.block_tables[batch.block_tables >= 0])
+    probe = np.random.default_rng(7).choice(used, size=min(16, used.size), replace=False)
+    assert np.array_equal(k[probe], batch.k_pool[probe]) and np.array_equal(v[probe], batch.v_pool[probe])
+    return dataclasses.replace(batch, k_pool=k, v_pool=v)
 
 
-def test_long_shared_sampled_rows(dev):
-    b = wl.config_long_shared()
-    note("long-context decode with shared prefixes: 16 x 32769 keys (4 rows)")
-    out, slots, t, plan = run_step(b, dev)
-    assert plan.num_merge > 0
+def run_whole(batch, dev, label, plan_check=None):
+    """The step on the device, then the append and every output element
+    against the oracle."""
+    t = to_device(batch, dev)
+    b = host_pools(batch, t)
+    out, slots, t, plan = run_step(b, dev, tensors=t)
+    if plan_check is not None:
+        plan_check(plan)
     check_append(b, slots, t)
-    rows = [0, 7, 8, 15]
-    ref = oracle.packed_attention_rows(b, rows)
-    check_attention(out[rows], np.stack([ref[r] for r in rows]), "long shared (sampled)")
+    del t
+    torch.cuda.empty_cache()
+    check_attention(out, oracle.packed_attention(b), label)
+
+
+def test_mixed_chunked_full(dev):
+    """Mixed chunked-prefill step, whole: 4 x 256 prefill rows after
+    prefixes 0/1024/2048/3072 and 1024 decode rows (2048 rows, every
+    element against the oracle)."""
+    note("mixed chunked-prefill step: 2048 rows (whole)")
+
+    def wide_and_narrow(plan):
+        assert plan.num_wide_items > 0 and plan.num_waves > 0
+
+    run_whole(wl.config_mixed_chunked(), dev, "mixed chunked (whole)", wide_and_narrow)
+
+
+def test_long_shared_full(dev):
+    """Long-context decode with shared prefixes, whole: 16 x 32769 keys,
+    two groups of 8 aliasing their first 128 blocks; contexts are split
+    over wavefronts and merged."""
+    note("long-context decode with shared prefixes: 16 x 32769 keys (whole)")
+
+    def merged(plan):
+        assert plan.num_merge > 0
+
+    run_whole(wl.config_long_shared(), dev, "long shared (whole)", merged)
 
 
 def test_prefill_chunk_sampled_rows(dev):
@@ -248,15 +279,41 @@ def test_wide_lists_with_interior_chunks(dev, opts):
 
 @pytest.mark.parametrize("scale", [0.01, 0.0883883, 0.3, 1.0])
 def test_softmax_scales(dev, scale):
-    """Scales other than 1/sqrt(128): up to that scale prefill tiles fold
-    scale * log2(e) into Q (one more bf16 rounding), above it they apply it
-    in fp32 like decode items; every case against the oracle at its scale."""
+    """Scales other than 1/sqrt(128), against the oracle at each scale:
+    prefill tiles and decode items both apply the scale in fp32 inside each
+    exponent's argument."""
     import dataclasses
     b = wl.make_batch("scales", [(300, 70), (0, 130), (900, 1), (64, 1)], seed=37)
     b = dataclasses.replace(b, scale=np.float32(scale))
     note(f"softmax scale {scale}")
     out, _, _, _ = run_step(b, dev)
     check_attention(out, oracle.packed_attention(b), f"scale {scale}")
+
+
+def _scaled_bits(bits, factor):
+    """bf16 bits of factor x value, rounded to nearest even (exact when the
+    factor is a power of two); NaN and infinity patterns are kept."""
+    x = np.asarray(bits, dtype=np.uint16)
+    special = (x & 0x7F80) == 0x7F80
+    y = wl.f32_to_bf16_bits((oracle.bf16_bits_to_f64(x) * factor).astype(np.float32))
+    return np.where(special, x, y).astype(np.uint16)
+
+
+@pytest.mark.parametrize("std", [2.0, 3.0])
+def test_large_queries_and_keys_at_the_default_scale(dev, std):
+    """Q and K drawn with standard deviation 2 and 3 instead of 1 (logits
+    4 and 9 times larger) at the default scale 1/sqrt(128): prefill tiles
+    and decode items both stay within the tolerance."""
+    b = wl.make_batch("large-qk", [(300, 70), (0, 130), (900, 1), (64, 1), (0, 600), (40, 3)], seed=38,
+                      pool="materialize")
+    b.q[:] = _scaled_bits(b.q, std)
+    b.k_new[:] = _scaled_bits(b.k_new, std)
+    b.k_pool[:] = _scaled_bits(b.k_pool, std)
+    note(f"Q/K std {std}")
+    out, slots, t, plan = run_step(b, dev)
+    assert plan.num_wide_items > 0
+    check_append(b, slots, t)
+    check_attention(out, oracle.packed_attention(b), f"Q/K std {std}")
 
 
 def test_nan_in_unused_slots_does_not_leak(dev):
@@ -301,6 +358,42 @@ def test_growing_scores_recompute(dev):
     check_attention(out, oracle.packed_attention(b), "growing scores")
 
 
+def test_growing_scores_with_large_values(dev):
+    """The growing-scores batch with every value multiplied by 2^30 (exact
+    in bf16): a tile whose probabilities still sum below the recompute bound
+    can then overflow its output accumulators (2^99 x 2^32 > 2^128), so the
+    accumulators must be checked too.  Scaling values by a power of two
+    scales the exact result by the same power, so the outputs divided by
+    2^30 must meet the usual tolerance."""
+    seqs = [(0, 3000), (2900, 100), (3100, 1)]
+    b = wl.make_batch("growing-scores-big-v", seqs, seed=35, pool="materialize")
+    D = b.head_dim
+    one = wl.f32_to_bf16_bits(np.float32(1.0))
+    b.q[:] = one
+    kval = lambda p: wl.f32_to_bf16_bits(np.float32(0.125 * (p // 32)))
+    cu = b.cu_seqlens_q
+    W = oracle.k_group(D)
+    for s, (c, ql) in enumerate(seqs):
+        for p in range(c):
+            blk = int(b.block_tables[s, p // 16])
+            b.k_pool[blk].reshape(b.num_kv_heads, D // W, 16, W)[:, :, p % 16, :] = kval(p)
+        for j in range(ql):
+            b.k_new[cu[s] + j] = kval(c + j)
+    big = 2.0 ** 30
+    b.v_pool[:] = _scaled_bits(b.v_pool, big)
+    b.v_new[:] = _scaled_bits(b.v_new, big)
+    note("growing scores, values x 2^30")
+    out, slots, t, plan = run_step(b, dev)
+    assert plan.num_wide_items > 0
+    check_append(b, slots, t)
+    got = oracle.bf16_bits_to_f64(out) / big
+    ref = oracle.packed_attention(b) / big
+    assert np.isfinite(got).all(), "non-finite output"
+    err = np.abs(got - ref)
+    note(f"growing scores x 2^30: max-abs {err.max():.3e} mean-abs {err.mean():.3e} (after / 2^30)")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+
+
 def test_attention_entry_points_agree(dev):
     """main + reduce called separately == the combined call == the step."""
     b = wl.config_decode64()
@@ -319,25 +412,43 @@ def test_attention_entry_points_agree(dev):
     check_attention(pkv.bf16_bits(o2), oracle.packed_attention(b), "split entry points")
 
 
-def test_trace_sampled_steps(dev):
-    """Steps of the continuous-batching trace (65,536-block pool): each
-    step's metadata with freshly drawn values; sampled rows of every kind."""
+@pytest.fixture(scope="module")
+def trace_steps():
     from synth import scheduler as sc
-    steps, _ = sc.continuous_batching_trace(sc.TraceConfig(steps=61))
-    rng = np.random.default_rng(9)
-    for i in (0, 1, 5, 60):
-        st = steps[i]
-        b = wl.batch_from_metadata(f"trace-step{i}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
-                                   65536, seed=149005 + 1000 * i)
-        note(f"trace step {i}: {b.num_rows} rows, {b.num_seqs} sequences")
-        out, slots, t, plan = run_step(b, dev)
-        check_append(b, slots, t)
-        cu = b.cu_seqlens_q
-        rows = set(rng.integers(0, b.num_rows, size=24).tolist())
-        for s in rng.integers(0, b.num_seqs, size=6):
-            rows |= {int(cu[s]), int(cu[s + 1]) - 1}
-        rows = sorted(rows)
-        ref = oracle.packed_attention_rows(b, rows)
-        check_attention(out[rows], np.stack([ref[r] for r in rows]), f"trace step {i} (sampled)")
-        del t
-        torch.cuda.empty_cache()
+    steps, _ = sc.continuous_batching_trace(sc.TraceConfig(steps=200))
+    return steps
+
+
+@pytest.mark.parametrize("index", [0, 5, 60, 150, 199])
+def test_trace_step_full(dev, trace_steps, index):
+    """Steps of the continuous-batching trace (65,536-block pool, 8192-token
+    budget), whole: each step's metadata with freshly drawn values, every
+    row of every kind against the oracle.  Step 0 is prefill only; steps
+    150 and 199 carry 700+ decode rows beside prefill chunks in a nearly
+    full pool."""
+    st = trace_steps[index]
+    b = wl.batch_from_metadata(f"trace-step{index}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
+                               65536, seed=149005 + 1000 * index)
+    note(f"trace step {index}: {b.num_rows} rows, {b.num_seqs} sequences, {st.n_decode} decode (whole)")
+    run_whole(b, dev, f"trace step {index} (whole)")
+
+
+def test_trace_steps_around_a_preemption(dev):
+    """The trace with a 16,384-block pool, where recompute preemption fires:
+    the step that evicts a request and the next one, in which the evicted
+    request is admitted again and prefills its prompt and generated tokens
+    from scratch, both compared whole."""
+    from synth import scheduler as sc
+    steps, sch = sc.continuous_batching_trace(sc.TraceConfig(steps=120, num_blocks=16384))
+    assert sch.preemptions > 0
+    first = next(st for st in steps if st.preempted)
+    victims = set(first.preempted)
+    again = next(st for st in steps[first.index + 1:]
+                 if any(rid in victims and cached == 0 for rid, cached, _ in st.rows))
+    for st in (first, again):
+        readmitted = [(rid, q) for rid, cached, q in st.rows if rid in victims and cached == 0]
+        note(f"preemption trace step {st.index}: {st.num_rows} rows, preempted {st.preempted}, "
+             f"re-admitted {readmitted}")
+        b = wl.batch_from_metadata(f"preempt-step{st.index}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
+                                   16384, seed=149500 + st.index)
+        run_whole(b, dev, f"preemption trace step {st.index} (whole)")
