@@ -268,6 +268,36 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
                    void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * pkv_paged_step with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a fixed array of
+ * PKV_STATIC_WS_BYTES (32 MiB) inside the library, one per GPU, held until
+ * the process ends; the call allocates nothing (no hipMalloc, no hipFree).
+ * Build the plan with pkv_plan(..., h_staging, ..., ws = NULL, ...); this
+ * call copies its plan->host_bytes of h_staging (host memory the caller
+ * owns; pinned lets the copy run asynchronously, and h_staging must then
+ * stay untouched until the copy has executed) into the array on `stream`,
+ * then runs pkv_paged_step on it.  Inputs, outputs and their meaning are
+ * those of pkv_paged_step.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents: calls on one stream are ordered,
+ * but calls that overlap on one GPU (two streams, or two host threads
+ * without ordering) race.  Errors: PKV_EWORKSPACE when plan->ws_bytes
+ * exceeds PKV_STATIC_WS_BYTES (checked before any device call), PKV_EINVAL
+ * for a null plan or staging buffer or a scale that is not positive and
+ * finite, PKV_ERANGE for a device index of 64 or more, and those of
+ * pkv_paged_step.
+ * ------------------------------------------------------------------------- */
+#define PKV_STATIC_WS_BYTES (32u << 20)
+int pkv_paged_step_static(const pkv_bf16 *q, const pkv_bf16 *k_new,
+                          const pkv_bf16 *v_new, pkv_bf16 *k_cache,
+                          pkv_bf16 *v_cache, const int32_t *cu_seqlens_q,
+                          const int32_t *seq_lens, const int32_t *block_tables,
+                          int32_t bt_stride, int64_t num_blocks,
+                          int64_t *slot_mapping, float scale,
+                          const pkv_plan_t *plan, const void *h_staging,
+                          pkv_bf16 *out, pkv_stream_t stream);
+
 /* ===========================================================================
  * The weight layers around the step: one packed layer.
  * ======================================================================== */

@@ -22,6 +22,8 @@ from .binding import (  # noqa: F401
     ROPE_THETA,
     pkv_paged_kv_append,
     pkv_paged_step,
+    pkv_paged_step_static,
+    STATIC_WS_BYTES,
     pkv_paged_varlen_attention,
     pkv_plan,
     pkv_slot_append,

@@ -81,6 +81,8 @@ _SIGNATURES = {
                                                   ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
     "pkv_paged_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
                                       ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_paged_step_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
+                                             ctypes.POINTER(PlanStruct), _P, _P, _P]),
     "pkv_linear": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "pkv_qkv_rope": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _P, _P, _P]),
     "pkv_layer_forward": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I64, _P, _F, _F,
@@ -387,6 +389,34 @@ def pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, bl
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
         _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], nb, _ptr(slot_mapping),
         float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
+    return out, slot_mapping
+
+
+STATIC_WS_BYTES = 32 << 20
+
+
+def pkv_paged_step_static(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, scale,
+                          plan: Plan, slot_mapping=None, out=None, stream=None):
+    """pkv_paged_step with the library's fixed device workspace: the plan's
+    host staging buffer is copied there by the call, and nothing is
+    allocated on the device by the library (plan.workspace is not used;
+    build the plan with host_only=True).  Calls that overlap on one GPU
+    share the array and race."""
+    lib = load_library()
+    dev, nb, out = _attn_args(q, k_cache, v_cache, block_tables, plan, out)
+    _need(k_new, "k_new", torch.bfloat16, dev)
+    _need(v_new, "v_new", torch.bfloat16, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seq_lens, "seq_lens", torch.int32, dev)
+    if slot_mapping is None:
+        slot_mapping = torch.empty(q.shape[0], dtype=torch.int64, device=dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    if plan.staging is None or plan.staging.device.type != "cpu":
+        raise ValueError("the plan needs its host staging buffer")
+    _check("pkv_paged_step_static", lib.pkv_paged_step_static(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+        _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1], nb, _ptr(slot_mapping),
+        float(scale), ctypes.byref(plan.st), _ptr(plan.staging), _ptr(out), _stream(stream, dev)))
     return out, slot_mapping
 
 

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cfloat>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -1212,6 +1213,38 @@ int check_plan(const pkv_plan_t *plan, size_t ws_bytes, const void *ws) {
   return PKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The fixed workspace of pkv_paged_step_static: a device array inside the
+// library, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it only stands for the
+// symbol); it looks up each device's address once, with that device
+// current, and uses that address for copies and kernel arguments.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticWsBytes = (size_t)PKV_STATIC_WS_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticWsBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on first use.
+int scratch_address(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERANGE;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PKV_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1427,6 +1460,29 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
   if (st != PKV_OK) return st;
   return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
                                     scale, plan, ws, ws_bytes, out, stream);
+}
+
+int pkv_paged_step_static(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                          pkv_bf16 *k_cache, pkv_bf16 *v_cache, const int32_t *cu_seqlens_q,
+                          const int32_t *seq_lens, const int32_t *block_tables, int32_t bt_stride,
+                          int64_t num_blocks, int64_t *slot_mapping, float scale,
+                          const pkv_plan_t *plan, const void *h_staging, pkv_bf16 *out,
+                          pkv_stream_t stream) {
+  // everything that needs no device is checked first
+  if (!plan || !valid_scale(scale)) return PKV_EINVAL;
+  if (plan->ws_bytes > kStaticWsBytes || plan->host_bytes > plan->ws_bytes) return PKV_EWORKSPACE;
+  if (plan->host_bytes > 0 && !h_staging) return PKV_EINVAL;
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != PKV_OK) return st;
+  // the plan's item lists, merge entries and zero tile; the partial results
+  // behind them are written by the attention launch before the merge reads
+  // them, so nothing else needs clearing
+  if (plan->host_bytes > 0 &&
+      hipMemcpyAsync(ws, h_staging, plan->host_bytes, hipMemcpyHostToDevice, as_stream(stream)) != hipSuccess)
+    return PKV_EHIP;
+  return pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, bt_stride,
+                        num_blocks, slot_mapping, scale, plan, ws, kStaticWsBytes, out, stream);
 }
 
 }  // extern "C"

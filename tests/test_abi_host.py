@@ -251,3 +251,21 @@ def test_entry_points_reject_a_scale_that_is_not_positive_and_finite(lib, scale)
                                               65536, fake, None) == want
         assert lib.pkv_paged_step(fake, fake, fake, fake, fake, fake, fake, fake, 1, 64, fake, f32(good),
                                   ctypes.byref(st), ws, 65536, fake, None) == want
+
+
+def test_static_step_rejects_a_plan_larger_than_its_array(lib):
+    """pkv_paged_step_static checks the plan's workspace size against its
+    fixed array before any device call (the pointers are never used)."""
+    assert pkv.STATIC_WS_BYTES == 32 << 20
+    st = binding.PlanStruct()
+    st.num_seqs, st.num_rows, st.num_q_heads, st.num_kv_heads, st.head_dim = 1, 1, 32, 8, 128
+    st.host_bytes = 4096
+    st.ws_bytes = pkv.STATIC_WS_BYTES + 256
+    fake = ctypes.c_void_p(256)
+    f32 = ctypes.c_float
+    args = [fake] * 8 + [1, 64, fake, f32(0.0883883), ctypes.byref(st)]
+    assert lib.pkv_paged_step_static(*args, fake, fake, None) == 4        # PKV_EWORKSPACE
+    st.ws_bytes = 8192
+    assert lib.pkv_paged_step_static(*args, None, fake, None) == 1        # no staging: PKV_EINVAL
+    args[11] = f32(float("nan"))
+    assert lib.pkv_paged_step_static(*args, fake, fake, None) == 1        # bad scale: PKV_EINVAL
