@@ -272,47 +272,58 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
 }
 
 // Few rows (M <= 64, a decode step): the product is bound by streaming the
-// weights, so the work is cut finer.  Workgroup b takes 32 features --
-// 16 of head b / 4 starting at 16 (b % 4) and their RoPE partners 64
-// further -- for all rows; its four wavefronts each take a quarter of the
-// inner dimension, loading their MFMA operands straight from memory (the
-// weights once, the few rows from L2), four 32-deep steps in flight, and
-// the quarters are summed through LDS.  Same D^T = W X^T layout as above,
-// with j = 0 the first 16 features and j = 1 their partners.
+// weights once, so the work is cut fine.  Workgroup b takes, for all rows,
+// with RoPE 32 features -- 16 of head b / 4 starting at 16 (b % 4) and
+// their partners 64 further, so a rotation needs no exchange -- else 16
+// consecutive features; its kWaves wavefronts each take an equal slice of
+// the inner dimension, loading their MFMA operands straight from memory (the
+// weights once, the few rows from L2), eight 32-deep steps in flight, and
+// the slices are summed through LDS.  Same D^T = W X^T layout as above, with
+// j = 0 the first 16 features and j = 1 their partners.  The rows are read
+// once per workgroup, so the 16-feature form (twice the workgroups, twice
+// the row reads per weight byte) pays only where the 32-feature one leaves
+// CUs idle: a 4096-wide layer's output projection takes 256 workgroups of
+// eight wavefronts (25 vs 30 us on MI355X), while its QKV projection keeps
+// 192 workgroups of 32 features (34.6 vs 48.6 us with 384 of 16).
 constexpr int kSkinnyRows = 64;
 constexpr int kSkinnyAhead = 8;
 
-template <bool kRope>
-__global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
-  __shared__ __attribute__((aligned(16))) float red[3][64][32];
+template <bool kRope, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void linear_skinny_kernel(LinearArgs g) {
+  constexpr int NJ = kRope ? 2 : 1;  // 16-feature tiles: the features, and with RoPE their partners
+  __shared__ __attribute__((aligned(16))) float red[kWaves - 1][64][16 * NJ];
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, r = lane & 15, gq = lane >> 4;
-  const int f0 = kHead * (b >> 2) + 16 * (b & 3);  // first feature; partners at f0 + 64
-  const int kq = g.K / 4, kbeg = wv * kq;
-  const uint16_t *wrow[2] = {g.w + (int64_t)(f0 + r) * g.K + 8 * gq, g.w + (int64_t)(f0 + 64 + r) * g.K + 8 * gq};
-  f32x4 acc[4][2];
+  const int f0 = kRope ? kHead * (b >> 2) + 16 * (b & 3) : 16 * b;  // first feature; partners at f0 + 64
+  const int kq = g.K / kWaves, kbeg = wv * kq;
+  const uint16_t *wrow[NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NJ; ++j) wrow[j] = g.w + (int64_t)(f0 + 64 * j + r) * g.K + 8 * gq;
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // rows past M read row M - 1 (their results are never stored), so every
   // load is unconditional and the loads of kSkinnyAhead steps stay in flight
   const uint16_t *xrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) xrow[i] = g.x + (int64_t)min(16 * i + r, g.M - 1) * g.K + 8 * gq;
-  auto load_step = [&](int k, u32x4 (&wa)[2], u32x4 (&xb)[4]) {
+  auto load_step = [&](int k, u32x4 (&wa)[NJ], u32x4 (&xb)[4]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wa[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[j] + k));
+    for (int j = 0; j < NJ; ++j) wa[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow[j] + k));
 #pragma unroll
     for (int i = 0; i < 4; ++i) xb[i] = *reinterpret_cast<const u32x4 *>(xrow[i] + k);
   };
-  auto mma = [&](const u32x4 (&wa)[2], const u32x4 (&xb)[4]) {
+  auto mma = [&](const u32x4 (&wa)[NJ], const u32x4 (&xb)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma(wa[j], xb[i], acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma(wa[j], xb[i], acc[i][j]);
   };
   const int nsteps = kq / 32;
   const int ngroups = nsteps / kSkinnyAhead;
-  u32x4 wa[kSkinnyAhead][2], xb[kSkinnyAhead][4];
+  u32x4 wa[kSkinnyAhead][NJ], xb[kSkinnyAhead][4];
   if (ngroups > 0) {
 #pragma unroll
     for (int a = 0; a < kSkinnyAhead; ++a) load_step(kbeg + 32 * a, wa[a], xb[a]);
@@ -331,25 +342,22 @@ __global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
     load_step(kbeg + 32 * st, wa[0], xb[0]);
     mma(wa[0], xb[0]);
   }
-  // sum the four quarters: wavefronts 1-3 park theirs in LDS, wavefront 0 adds
+  // sum the slices: wavefronts 1.. park theirs in LDS, wavefront 0 adds
   if (wv > 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[wv - 1][16 * i + r][16 * j + 4 * gq + e] = acc[i][j][e];
+      for (int j = 0; j < NJ; ++j)
+        *reinterpret_cast<f32x4 *>(&red[wv - 1][16 * i + r][16 * j + 4 * gq]) = acc[i][j];
   }
   __syncthreads();
   if (wv > 0) return;
-#pragma unroll
-  for (int q = 0; q < 3; ++q)
+#pragma unroll 1
+  for (int q = 0; q < kWaves - 1; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] += red[q][16 * i + r][16 * j + 4 * gq + e];
+      for (int j = 0; j < NJ; ++j) acc[i][j] += *reinterpret_cast<const f32x4 *>(&red[q][16 * i + r][16 * j + 4 * gq]);
 
   uint16_t *dst = g.y;
   int64_t row_stride = g.N, col0 = f0;
@@ -377,20 +385,23 @@ __global__ __launch_bounds__(256) void linear_skinny_kernel(LinearArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int m = 16 * i + r;
     if (m >= g.M) continue;
-    f32x4 o0 = acc[i][0], o1 = acc[i][1];
-    if (kRope && rotate) {
-      const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float c, sn;
-        rope_cos_sin(p, f[e], c, sn);
-        o0[e] = acc[i][0][e] * c - acc[i][1][e] * sn;
-        o1[e] = acc[i][1][e] * c + acc[i][0][e] * sn;
-      }
-    }
     uint16_t *dr = dst + (int64_t)m * row_stride + col0 + 4 * gq;
+    f32x4 o0 = acc[i][0];
+    if constexpr (kRope) {
+      f32x4 o1 = acc[i][1];
+      if (rotate) {
+        const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float c, sn;
+          rope_cos_sin(p, f[e], c, sn);
+          o0[e] = acc[i][0][e] * c - acc[i][1][e] * sn;
+          o1[e] = acc[i][1][e] * c + acc[i][0][e] * sn;
+        }
+      }
+      *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+    }
     *reinterpret_cast<u32x2 *>(dr) = u32x2{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
-    *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
   }
 }
 
@@ -398,11 +409,17 @@ inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s
 
 int launch_linear(LinearArgs g, bool rope, pkv_stream_t stream) {
   if (g.M <= kSkinnyRows && g.K % 128 == 0) {
-    const dim3 grid((unsigned)(g.N / 32));
-    if (rope)
-      hipLaunchKernelGGL(linear_skinny_kernel<true>, grid, dim3(256), 0, as_stream(stream), g);
-    else
-      hipLaunchKernelGGL(linear_skinny_kernel<false>, grid, dim3(256), 0, as_stream(stream), g);
+    if (rope) {
+      hipLaunchKernelGGL((linear_skinny_kernel<true, 4>), dim3((unsigned)(g.N / 32)), dim3(256), 0,
+                         as_stream(stream), g);
+    } else if (g.N / 16 <= kCUs && g.K % 256 == 0) {
+      // every workgroup resident at once, one per CU
+      hipLaunchKernelGGL((linear_skinny_kernel<false, 8>), dim3((unsigned)(g.N / 16)), dim3(512), 0,
+                         as_stream(stream), g);
+    } else {
+      hipLaunchKernelGGL((linear_skinny_kernel<false, 4>), dim3((unsigned)(g.N / 16)), dim3(256), 0,
+                         as_stream(stream), g);
+    }
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
   }
   // 256-row or 128-row tiles, whichever takes fewer rounds of one

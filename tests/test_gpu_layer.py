@@ -58,7 +58,7 @@ def _close(got_bits, ref, label):
     assert (err <= bound).all(), (label, float(err.max()))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (64, 384, 4096), (65, 256, 256), (300, 384, 512),
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (64, 384, 4096), (5, 4096, 4096), (65, 256, 256), (300, 384, 512),
                                    (513, 128, 4096), (4096, 4096, 64), (4000, 4224, 128)])
 def test_linear_matches_oracle(dev, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
@@ -83,9 +83,10 @@ def test_linear_rejects_unsupported_shapes(dev):
     ("worked", [(0, 5), (7, 1), (3, 1)]),
     ("chunks-and-decode", [(30720, 70), (0, 33), (5000, 1), (4095, 1), (1, 2)]),
     ("long-prefill", [(0, 1500), (100, 547), (9000, 1)]),
+    ("decode-h384", [(5000, 1), (10, 1), (0, 3), (77, 1)]),   # few rows, hidden 384: four-wavefront form
 ])
 def test_qkv_rope_matches_oracle(dev, name, seqs):
-    hidden, Hq, Hkv = (64 if name == "long-prefill" else 512), 32, 8
+    hidden, Hq, Hkv = {"long-prefill": 64, "decode-h384": 384}.get(name, 512), 32, 8
     cu = np.concatenate([[0], np.cumsum([n for _, n in seqs])]).astype(np.int32)
     sl = np.array([c + n for c, n in seqs], dtype=np.int32)
     T = int(cu[-1])
