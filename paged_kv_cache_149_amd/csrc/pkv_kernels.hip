@@ -145,14 +145,44 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Sequence of packed row t0 (the last s with cu[s] <= t0; cu[S] = T > t0),
+// found by one wavefront in rounds of 64 probes: each round narrows the
+// candidates to one 64th with one coalesced load, so S + 1 entries take
+// ceil(log64(S + 1)) dependent loads (two up to 4,095 sequences) where a
+// binary search takes log2(S + 1).  Lane 0 always probes cu[lo] <= t0 (cu[0]
+// = 0), so every ballot has a bit set; every probe is clamped into cu[0 .. S].
+// ---------------------------------------------------------------------------
+__device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int t0, int lane) {
+  int lo = 0, len = S + 1;  // the answer lies in cu[lo .. lo + len)
+  while (len > 64) {
+    const int step = (len + 63) / 64;
+    const bool le = lane * step < len && cu[min(lo + lane * step, S)] <= t0;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(le);
+    const int last = m ? 63 - __builtin_clzll(m) : 0;  // m == 0 only for malformed metadata
+    lo += last * step;
+    len = min(step, len - last * step);
+  }
+  const bool le = lane < len && cu[min(lo + lane, S)] <= t0;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(le);
+  return min(m ? lo + 63 - __builtin_clzll(m) : lo, S - 1);
+}
+
+// ---------------------------------------------------------------------------
 // append: a workgroup per 16 consecutive packed rows and one kv head, a
-// thread per (row, 8 dimensions) for K and for V.  K rows: lanes run over
-// dimensions, each row's 256 bytes are four 64-byte stores, one per
-// 32-dimension group of the tile.  V tiles are dimension-major (a block's 16 tokens
-// contiguous per dimension): lanes run over rows, so each 2-byte store
-// instruction writes, per dimension, the consecutive slots of up to 16
-// consecutive rows -- whole sectors inside any prefill run, whatever its
-// alignment; decode rows touch one slot of a block each.
+// thread per (row, 8 dimensions) for K and for V.  The rows' K and V are
+// loaded first, so their latency overlaps the slot translation.  Slots: the
+// first row's sequence s0 by the 64-way search above (wavefront 0), then a
+// window of 64 cu entries after s0 gives every row of the group its
+// sequence by counting (cu is non-decreasing, so the entries <= t form a
+// prefix of the window); a row more than 63 sequence boundaries past the
+// first -- only possible across empty sequences -- takes the plain binary
+// search.  K rows: lanes run over dimensions, each row's 256 bytes are four
+// 64-byte stores, one per 32-dimension group of the tile.  V tiles are
+// dimension-major (a block's 16 tokens contiguous per dimension): lanes run
+// over rows, so each store instruction writes, per dimension, the
+// consecutive slots of up to 16 consecutive rows -- whole sectors inside any
+// prefill run, whatever its alignment; decode rows touch one slot of a block
+// each.
 // ---------------------------------------------------------------------------
 constexpr int kAppendRows = 16;
 
@@ -164,62 +194,89 @@ __global__ __launch_bounds__(256) void append_kernel(
     int64_t num_blocks, int64_t *__restrict__ slot_out, uint16_t *__restrict__ kc,
     uint16_t *__restrict__ vc) {
   __shared__ int64_t srow[kAppendRows];
+  __shared__ uint32_t vrow[kAppendRows][D / 2 + 1];  // +1: rows start in different banks
   const int t0 = blockIdx.x * kAppendRows;
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  if (tid < kAppendRows) {
-    const int t = t0 + tid;
-    int64_t sl = -1;
-    if (t < T) {
-      if (slot_in) {
-        sl = slot_in[t];
-        if (sl < 0 || sl >= num_blocks * pkv::kBlock) sl = -1;
-      } else {
-        sl = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
-        if (h == 0) slot_out[t] = sl;
+  const int ri = tid >> 4, d0 = 8 * (tid & 15);  // this thread's row and dimensions
+  const bool row_ok = t0 + ri < T;
+  // the rows' K (kept in registers) and V (staged in LDS), before the slots
+  u32x4 xk = u32x4{0, 0, 0, 0};
+  if (row_ok) {
+    xk = load16(k_new + ((int64_t)(t0 + ri) * Hkv + h) * D + d0);
+    const u32x4 xv = load16(v_new + ((int64_t)(t0 + ri) * Hkv + h) * D + d0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vrow[ri][d0 / 2 + e] = xv[e];
+  }
+  if (tid < 64) {
+    const int lane = tid;
+    if (slot_in) {
+      if (lane < kAppendRows) {
+        int64_t sl = -1;
+        if (t0 + lane < T) {
+          sl = slot_in[t0 + lane];
+          if (sl < 0 || sl >= num_blocks * pkv::kBlock) sl = -1;
+        }
+        srow[lane] = sl;
+      }
+    } else {
+      const int s0 = wave_seq_of_row(cu, S, t0, lane);
+      // window: cu[s0 + 1 + l] (clamped at cu[S] = T, which no row reaches)
+      const int w = cu[min(s0 + 1 + lane, S)];
+      int cnt = 0;  // lane i < 16: window entries <= row t0 + i
+#pragma unroll
+      for (int i = 0; i < kAppendRows; ++i) {
+        const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64(w <= t0 + i));
+        if (lane == i) cnt = c;
+      }
+      const int cu_s0 = cu[s0];
+      // cu[s] and cu[s + 1] of this lane's row, from the window
+      const int lo_e = __shfl(w, max(cnt - 1, 0)), hi_e = __shfl(w, min(cnt, 63));
+      if (lane < kAppendRows) {
+        const int t = t0 + lane;
+        int64_t sl = -1;
+        if (t < T) {
+          if (cnt < 64) {
+            const int sq = min(s0 + cnt, S - 1);  // S - 1 unless the metadata is malformed
+            const int c_lo = cnt == 0 ? cu_s0 : lo_e;
+            const int pos = seq_lens[sq] - (hi_e - c_lo) + (t - c_lo);
+            if (pos >= 0 && (pos >> 4) < bt_stride) {
+              const int b = bt[(int64_t)sq * bt_stride + (pos >> 4)];
+              if (b >= 0 && b < num_blocks) sl = (int64_t)b * pkv::kBlock + (pos & 15);
+            }
+          } else {
+            sl = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
+          }
+          if (h == 0) slot_out[t] = sl;
+        }
+        srow[lane] = sl;
       }
     }
-    srow[tid] = sl;
   }
   __syncthreads();
   {  // K: lanes over dimensions
-    const int i = tid >> 4, d0 = 8 * (tid & 15);
-    const int64_t sl = srow[i];
-    if (t0 + i < T && sl >= 0) {
-      const u32x4 x = load16(k_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
+    const int64_t sl = srow[ri];
+    if (row_ok && sl >= 0)
       *reinterpret_cast<u32x4 *>(kc + ((sl >> 4) * Hkv + h) * TILE + (d0 / kKGroup) * kKGroupElems +
-                                 (sl & 15) * kKGroup + d0 % kKGroup) = x;
-    }
+                                 (sl & 15) * kKGroup + d0 % kKGroup) = xk;
   }
-  {  // V: the 16 rows through LDS, then written dimension-major: lanes over
-     // (row pair, dimension), pairs fastest, so a wavefront's stores cover
-     // 8 dimensions x 16 tokens -- 32 contiguous bytes per dimension when
-     // the rows fill a block in order; a pair of consecutive, 4-byte-aligned
-     // slots is one 4-byte store
-    __shared__ uint32_t vrow[kAppendRows][D / 2 + 1];  // +1: rows start in different banks
-    {
-      const int i = tid >> 4, d0 = 8 * (tid & 15);
-      if (t0 + i < T) {
-        const u32x4 x = load16(v_new + ((int64_t)(t0 + i) * Hkv + h) * D + d0);
+  // V, dimension-major: lanes over (row pair, dimension), pairs fastest, so a
+  // wavefront's stores cover 8 dimensions x 16 tokens -- 32 contiguous bytes
+  // per dimension when the rows fill a block in order; a pair of
+  // consecutive, 4-byte-aligned slots is one 4-byte store
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vrow[i][d0 / 2 + e] = x[e];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kAppendRows * D / 2 / 256; ++k) {
-      const int u = tid + 256 * k, p = u & 7, d = u >> 3;
-      const int r0 = 2 * p, r1 = r0 + 1;
-      const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
-      const uint32_t w0 = vrow[r0][d >> 1], w1 = vrow[r1][d >> 1];
-      const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
-      if (s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0) {
-        *reinterpret_cast<uint32_t *>(vc + ((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)) =
-            a0 | (a1 << 16);
-      } else {
-        if (s0 >= 0) vc[((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)] = (uint16_t)a0;
-        if (s1 >= 0) vc[((s1 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s1 & 15)] = (uint16_t)a1;
-      }
+  for (int k = 0; k < kAppendRows * D / 2 / 256; ++k) {
+    const int u = tid + 256 * k, p = u & 7, d = u >> 3;
+    const int r0 = 2 * p, r1 = r0 + 1;
+    const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
+    const uint32_t w0 = vrow[r0][d >> 1], w1 = vrow[r1][d >> 1];
+    const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
+    if (s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0) {
+      *reinterpret_cast<uint32_t *>(vc + ((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)) =
+          a0 | (a1 << 16);
+    } else {
+      if (s0 >= 0) vc[((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)] = (uint16_t)a0;
+      if (s1 >= 0) vc[((s1 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s1 & 15)] = (uint16_t)a1;
     }
   }
 }

@@ -228,6 +228,9 @@ EDGE = {
     "short-prefills": [(0, 2), (3, 3), (10, 4), (0, 5), (100, 7)],
     "long-prefill": [(50, 100), (0, 130)],
     "ragged-tail": [(1023, 1), (0, 65), (4000, 17), (3, 1)],
+    # rows of one 16-row append group more than 63 sequence boundaries apart
+    # (runs of empty sequences): the slot translation's fallback search
+    "many-empty-seqs": [(3, 1)] + [(7, 0)] * 80 + [(30, 2)] + [(1, 0)] * 70 + [(0, 5), (40, 1)] + [(2, 0)] * 3000,
 }
 
 
