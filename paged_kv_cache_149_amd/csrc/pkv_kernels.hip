@@ -168,13 +168,14 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 }
 
 // ---------------------------------------------------------------------------
-// append: a workgroup per 16 consecutive packed rows and one kv head, a
-// thread per (row, 8 dimensions) for K and for V.  The rows' K and V are
-// loaded first, so their latency overlaps the slot translation.  Slots: the
-// first row's sequence s0 by the 64-way search above (wavefront 0), then a
-// window of 64 cu entries after s0 gives every row of the group its
-// sequence by counting (cu is non-decreasing, so the entries <= t form a
-// prefix of the window); a row more than 63 sequence boundaries past the
+// append: a workgroup per 16 consecutive packed rows and up to four kv
+// heads, a thread per (row, 8 dimensions) for the K and the V of each head.
+// All the rows' K and V are loaded first, so their latency overlaps the
+// slot translation, which the workgroup does once for its four heads.
+// Slots: the first row's sequence s0 by the 64-way search above (wavefront
+// 0), then a window of 64 cu entries after s0 gives every row of the group
+// its sequence by counting (cu is non-decreasing, so the entries <= t form
+// a prefix of the window); a row more than 63 sequence boundaries past the
 // first -- only possible across empty sequences -- takes the plain binary
 // search.  K rows: lanes run over dimensions, each row's 256 bytes are four
 // 64-byte stores, one per 32-dimension group of the tile.  V tiles are
@@ -185,6 +186,7 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 // each.
 // ---------------------------------------------------------------------------
 constexpr int kAppendRows = 16;
+constexpr int kAppendHeads = 4;
 
 __global__ __launch_bounds__(256) void append_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
@@ -194,19 +196,30 @@ __global__ __launch_bounds__(256) void append_kernel(
     int64_t num_blocks, int64_t *__restrict__ slot_out, uint16_t *__restrict__ kc,
     uint16_t *__restrict__ vc) {
   __shared__ int64_t srow[kAppendRows];
-  __shared__ uint32_t vrow[kAppendRows][D / 2 + 1];  // +1: rows start in different banks
+  __shared__ uint32_t vrow[kAppendHeads][kAppendRows][D / 2 + 1];  // +1: rows start in different banks
   const int t0 = blockIdx.x * kAppendRows;
-  const int h = blockIdx.y;
+  const int h0 = blockIdx.y * kAppendHeads;
+  const int nh = min(kAppendHeads, Hkv - h0);
   const int tid = threadIdx.x;
   const int ri = tid >> 4, d0 = 8 * (tid & 15);  // this thread's row and dimensions
   const bool row_ok = t0 + ri < T;
   // the rows' K (kept in registers) and V (staged in LDS), before the slots
-  u32x4 xk = u32x4{0, 0, 0, 0};
+  u32x4 xk[kAppendHeads];
   if (row_ok) {
-    xk = load16(k_new + ((int64_t)(t0 + ri) * Hkv + h) * D + d0);
-    const u32x4 xv = load16(v_new + ((int64_t)(t0 + ri) * Hkv + h) * D + d0);
+    const int64_t base = ((int64_t)(t0 + ri) * Hkv + h0) * D + d0;
+    u32x4 xv[kAppendHeads];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vrow[ri][d0 / 2 + e] = xv[e];
+    for (int j = 0; j < kAppendHeads; ++j) {
+      if (j < nh) {
+        xk[j] = load16(k_new + base + j * D);
+        xv[j] = load16(v_new + base + j * D);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kAppendHeads; ++j)
+      if (j < nh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vrow[j][ri][d0 / 2 + e] = xv[j][e];
   }
   if (tid < 64) {
     const int lane = tid;
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(256) void append_kernel(
           } else {
             sl = row_slot(cu, seq_lens, bt, bt_stride, S, t, num_blocks);
           }
-          if (h == 0) slot_out[t] = sl;
+          if (blockIdx.y == 0) slot_out[t] = sl;
         }
         srow[lane] = sl;
       }
@@ -256,27 +269,34 @@ __global__ __launch_bounds__(256) void append_kernel(
   __syncthreads();
   {  // K: lanes over dimensions
     const int64_t sl = srow[ri];
-    if (row_ok && sl >= 0)
-      *reinterpret_cast<u32x4 *>(kc + ((sl >> 4) * Hkv + h) * TILE + (d0 / kKGroup) * kKGroupElems +
-                                 (sl & 15) * kKGroup + d0 % kKGroup) = xk;
+    if (row_ok && sl >= 0) {
+      uint16_t *kp = kc + ((sl >> 4) * Hkv + h0) * TILE + (d0 / kKGroup) * kKGroupElems + (sl & 15) * kKGroup +
+                     d0 % kKGroup;
+#pragma unroll
+      for (int j = 0; j < kAppendHeads; ++j)
+        if (j < nh) *reinterpret_cast<u32x4 *>(kp + j * TILE) = xk[j];
+    }
   }
   // V, dimension-major: lanes over (row pair, dimension), pairs fastest, so a
   // wavefront's stores cover 8 dimensions x 16 tokens -- 32 contiguous bytes
   // per dimension when the rows fill a block in order; a pair of
   // consecutive, 4-byte-aligned slots is one 4-byte store
+  const int p = tid & 7;  // this thread's row pair, the same in every round below
+  const int r0 = 2 * p, r1 = r0 + 1;
+  const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
+  const bool pair = s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0;
 #pragma unroll
-  for (int k = 0; k < kAppendRows * D / 2 / 256; ++k) {
-    const int u = tid + 256 * k, p = u & 7, d = u >> 3;
-    const int r0 = 2 * p, r1 = r0 + 1;
-    const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
-    const uint32_t w0 = vrow[r0][d >> 1], w1 = vrow[r1][d >> 1];
+  for (int k = 0; k < kAppendHeads * kAppendRows * D / 2 / 256; ++k) {
+    const int u = tid + 256 * k, d = (u >> 3) & (D - 1), j = u >> 10;
+    if (j >= nh) continue;
+    const uint32_t w0 = vrow[j][r0][d >> 1], w1 = vrow[j][r1][d >> 1];
     const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
-    if (s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0) {
-      *reinterpret_cast<uint32_t *>(vc + ((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)) =
-          a0 | (a1 << 16);
+    uint16_t *vh = vc + (int64_t)(h0 + j) * TILE + (int64_t)d * pkv::kBlock;
+    if (pair) {
+      *reinterpret_cast<uint32_t *>(vh + (s0 >> 4) * Hkv * TILE + (s0 & 15)) = a0 | (a1 << 16);
     } else {
-      if (s0 >= 0) vc[((s0 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s0 & 15)] = (uint16_t)a0;
-      if (s1 >= 0) vc[((s1 >> 4) * Hkv + h) * TILE + (int64_t)d * pkv::kBlock + (s1 & 15)] = (uint16_t)a1;
+      if (s0 >= 0) vh[(s0 >> 4) * Hkv * TILE + (s0 & 15)] = (uint16_t)a0;
+      if (s1 >= 0) vh[(s1 >> 4) * Hkv * TILE + (s1 & 15)] = (uint16_t)a1;
     }
   }
 }
@@ -1346,7 +1366,7 @@ int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
   if (head_dim != D) return PKV_EUNSUPPORTED;
   if (num_rows == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
-  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, num_kv_heads);
+  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, (num_kv_heads + kAppendHeads - 1) / kAppendHeads);
   hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, slot_mapping,
                      nullptr, nullptr, nullptr, 0, 0, num_rows, num_kv_heads, num_blocks, nullptr,
                      k_cache, v_cache);
@@ -1497,7 +1517,7 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t 
   if (!k_new || !v_new || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables ||
       !slot_mapping || num_seqs == 0)
     return PKV_EINVAL;
-  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, num_kv_heads);
+  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, (num_kv_heads + kAppendHeads - 1) / kAppendHeads);
   hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, nullptr,
                      cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs, num_rows, num_kv_heads,
                      num_blocks, slot_mapping, k_cache, v_cache);
