@@ -168,10 +168,11 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 }
 
 // ---------------------------------------------------------------------------
-// append: a workgroup per 16 consecutive packed rows and up to four kv
-// heads, a thread per (row, 8 dimensions) for the K and the V of each head.
-// All the rows' K and V are loaded first, so their latency overlaps the
-// slot translation, which the workgroup does once for its four heads.
+// append: a workgroup per 16 consecutive packed rows and kHeads kv heads
+// (four for large steps, one when the rows are too few to fill the GPU), a
+// thread per (row, 8 dimensions) for the K and the V of each head.  All the
+// rows' K and V are loaded first, so their latency overlaps the slot
+// translation, which the workgroup does once for its heads.
 // Slots: the first row's sequence s0 by the 64-way search above (wavefront
 // 0), then a window of 64 cu entries after s0 gives every row of the group
 // its sequence by counting (cu is non-decreasing, so the entries <= t form
@@ -186,8 +187,8 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 // each.
 // ---------------------------------------------------------------------------
 constexpr int kAppendRows = 16;
-constexpr int kAppendHeads = 4;
 
+template <int kAppendHeads>
 __global__ __launch_bounds__(256) void append_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     const int64_t *__restrict__ slot_in,  // given slots, or null: translate
@@ -1280,6 +1281,22 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? PKV_OK : P
 // scale commutes with.
 inline bool valid_scale(float scale) { return scale > 0.f && scale <= FLT_MAX; }
 
+// Four kv heads per append workgroup once the 16-row groups alone give 256
+// workgroups or more; one otherwise, so a small step still spreads over the
+// GPU (64 decode rows: 32 workgroups instead of 8).
+void launch_append(const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_in, const int32_t *cu,
+                   const int32_t *seq_lens, const int32_t *bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
+                   int64_t num_blocks, int64_t *slot_out, uint16_t *kc, uint16_t *vc, hipStream_t stream) {
+  const unsigned groups = (unsigned)((T + kAppendRows - 1) / kAppendRows);
+  if (groups >= 256) {
+    hipLaunchKernelGGL(append_kernel<4>, dim3(groups, (Hkv + 3) / 4), dim3(256), 0, stream, k_new, v_new, slot_in, cu,
+                       seq_lens, bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc);
+  } else {
+    hipLaunchKernelGGL(append_kernel<1>, dim3(groups, Hkv), dim3(256), 0, stream, k_new, v_new, slot_in, cu, seq_lens,
+                       bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc);
+  }
+}
+
 int check_plan(const pkv_plan_t *plan, size_t ws_bytes, const void *ws) {
   if (!plan) return PKV_EINVAL;
   if (plan->head_dim != D || plan->num_q_heads <= 0 || plan->num_kv_heads <= 0) return PKV_EINVAL;
@@ -1366,10 +1383,8 @@ int pkv_paged_kv_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
   if (head_dim != D) return PKV_EUNSUPPORTED;
   if (num_rows == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
-  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, (num_kv_heads + kAppendHeads - 1) / kAppendHeads);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, slot_mapping,
-                     nullptr, nullptr, nullptr, 0, 0, num_rows, num_kv_heads, num_blocks, nullptr,
-                     k_cache, v_cache);
+  launch_append(k_new, v_new, slot_mapping, nullptr, nullptr, nullptr, 0, 0, num_rows, num_kv_heads, num_blocks,
+                nullptr, k_cache, v_cache, as_stream(stream));
   return launch_status();
 }
 
@@ -1517,10 +1532,8 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t 
   if (!k_new || !v_new || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables ||
       !slot_mapping || num_seqs == 0)
     return PKV_EINVAL;
-  const dim3 grid((num_rows + kAppendRows - 1) / kAppendRows, (num_kv_heads + kAppendHeads - 1) / kAppendHeads);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, as_stream(stream), k_new, v_new, nullptr,
-                     cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs, num_rows, num_kv_heads,
-                     num_blocks, slot_mapping, k_cache, v_cache);
+  launch_append(k_new, v_new, nullptr, cu_seqlens_q, seq_lens, block_tables, bt_stride, num_seqs, num_rows,
+                num_kv_heads, num_blocks, slot_mapping, k_cache, v_cache, as_stream(stream));
   return launch_status();
 }
 
