@@ -32,6 +32,8 @@
 // same lane, and the rotation needs no data exchange.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
@@ -284,7 +286,9 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinearArgs g) {
 // the row reads per weight byte) pays only where the 32-feature one leaves
 // CUs idle: a 4096-wide layer's output projection takes 256 workgroups of
 // eight wavefronts (25 vs 30 us on MI355X), while its QKV projection keeps
-// 192 workgroups of 32 features (34.6 vs 48.6 us with 384 of 16).
+// 192 workgroups of 32 features (34.6 vs 48.6 us with 384 of 16).  An inner
+// dimension that is a multiple of 256 takes the LDS-staged form below
+// instead; this one covers the rest (multiples of 128).
 constexpr int kSkinnyRows = 64;
 constexpr int kSkinnyAhead = 8;
 
@@ -405,9 +409,225 @@ __global__ __launch_bounds__(64 * kWaves) void linear_skinny_kernel(LinearArgs g
   }
 }
 
+// Few rows (M <= 64) with an inner dimension a multiple of 256: the same
+// split of the features as above, eight wavefronts per workgroup, but the
+// operands go through LDS.  Read straight into MFMA operands, every load of
+// the rows takes 64 bytes from each of 16 rows, and the rows' L2 traffic
+// (all of the rows for every workgroup) runs at that scattered pattern's
+// rate, about half of what 1 KiB contiguous loads reach.  Here the
+// workgroup copies each 256-deep chunk of the rows (64 rows x 512 bytes)
+// into an LDS ring by direct global->LDS loads of 1 KiB contiguous each (two
+// rows), and the weights of the chunk beside them in MFMA operand order (a
+// 1 KiB region per feature tile and 32-deep step); the wavefronts read
+// their operands from there.  A row's 16-byte pieces are stored
+// XOR-swizzled by the row's low four bits, so the 16 rows of one operand
+// read fall on distinct banks.  Wavefront w takes feature tile w % NJ and
+// 32-deep steps of each chunk by k-group w / NJ, and the k-groups' sums meet
+// in LDS.  The ring holds three chunks: the one being read, and two in
+// flight.  At 64 rows and hidden 4096 on MI355X: QKV with RoPE 35.6 -> 27.2
+// us, the output projection 25.3 -> 18.5 us against the form above.
+constexpr int kXChunk = 256;                  // inner dimension per staged chunk
+constexpr int kXChunkVec = 64 * kXChunk / 8;  // u32x4 of a chunk's rows (32 KiB)
+constexpr int kXRing = 3;                     // chunk buffers
+
+template <int kVm>
+__device__ __forceinline__ void layer_wait_vmcnt() {
+  // s_waitcnt vmcnt(kVm), expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((kVm & 0xF) | (7 << 4) | (15 << 8) | ((kVm >> 4) << 14));
+}
+
+template <bool kRope>
+__device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  constexpr int NJ = kRope ? 2 : 1;           // feature tiles: the features, and with RoPE their partners 64 further
+  constexpr int KG = 8 / NJ;                  // k-groups
+  constexpr int SPW = NJ;                     // 32-deep steps per wavefront and chunk (8 per chunk / KG)
+  constexpr int kSlotVec = kXChunkVec + NJ * 8 * 64;  // u32x4 per ring slot: rows, then weight regions
+  constexpr int kLoads = 4 + NJ;              // global->LDS loads per wavefront and chunk
+  __shared__ __attribute__((aligned(16))) u32x4 ring[kXRing * kSlotVec];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int jt = w % NJ, kg = w / NJ;
+  const int f0 = kRope ? kHead * (b >> 2) + 16 * (b & 3) : 16 * b;  // first feature; partners at f0 + 64
+  const int nch = g.K / kXChunk;
+
+  // this wavefront's copies of a chunk: rows 8w + 2q and 8w + 2q + 1 (q < 4),
+  // lane l taking piece (l % 32) ^ (row % 16) of row 8w + 2q + l / 32 (rows
+  // past M read row M - 1: never stored); weight regions (tile, step) =
+  // (e / 8, e % 8) for e = NJ w + q (q < NJ), lane (r, gq) taking the
+  // 16 bytes at dimension 32 step + 8 gq of feature f0 + 64 tile + r
+  const uint16_t *xsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * w + 2 * q + (lane >> 5);
+    xsrc[q] = g.x + (int64_t)min(row, g.M - 1) * g.K + 8 * ((lane & 31) ^ (row & 15));
+  }
+  const uint16_t *wsrc[NJ];
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    const int e = NJ * w + q;
+    wsrc[q] = g.w + (int64_t)(f0 + 64 * (e >> 3) + r) * g.K + 32 * (e & 7) + 8 * gq;
+  }
+  auto issue = [&](int c, int slot) {
+    u32x4 *base = ring + slot * kSlotVec;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(xsrc[q] + kXChunk * c, (lds_void_t *)(base + w * 4 * 64 + 64 * q), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NJ; ++q)
+      __builtin_amdgcn_global_load_lds(wsrc[q] + kXChunk * c, (lds_void_t *)(base + kXChunkVec + (NJ * w + q) * 64),
+                                       16, 0, 0);
+  };
+  // LDS byte addresses (slot 0) of this lane's operands of step t: the rows'
+  // piece 4 st + gq of row r (row tile 0) stored at (4 st + gq) ^ r, the
+  // weights' region (jt, st)
+  uint32_t xaddr[SPW], waddr[SPW];
+#pragma unroll
+  for (int t = 0; t < SPW; ++t) {
+    const int st = kg * SPW + t;
+    const __attribute__((address_space(3))) u32x4 *lds = (const __attribute__((address_space(3))) u32x4 *)ring;
+    xaddr[t] = (uint32_t)(uintptr_t)(lds + r * 32 + ((4 * st + gq) ^ r));
+    waddr[t] = (uint32_t)(uintptr_t)(lds + kXChunkVec + (8 * jt + st) * 64 + lane);
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot) {
+    const uint32_t off = (uint32_t)(slot * kSlotVec * 16);
+    u32x4 xb[SPW][4], wv[SPW];
+#pragma unroll
+    for (int t = 0; t < SPW; ++t) {
+      const uint32_t xa = xaddr[t] + off, wa = waddr[t] + off;
+      asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(wv[t]) : "v"(wa));
+      asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(xb[t][0]) : "v"(xa));
+      asm volatile("ds_read_b128 %0, %1 offset:8192" : "=v"(xb[t][1]) : "v"(xa));
+      asm volatile("ds_read_b128 %0, %1 offset:16384" : "=v"(xb[t][2]) : "v"(xa));
+      asm volatile("ds_read_b128 %0, %1 offset:24576" : "=v"(xb[t][3]) : "v"(xa));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < SPW; ++t) {
+      asm volatile("" : "+v"(wv[t]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(xb[t][i]));
+        acc[i] = mfma(wv[t], xb[t][i], acc[i]);
+      }
+    }
+  };
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Chunk c is copied into slot c % 3 two chunks ahead, after the barrier
+  // that follows everyone's reads of chunk c - 1 (the slot's previous
+  // chunk).  Loads complete in order: at chunk c only chunk c + 1's
+  // kLoads loads may still fly behind it.
+  issue(0, 0);
+  if (nch > 1) issue(1, 1);
+  int slot = 0;
+  for (int c = 0; c < nch; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < nch) layer_wait_vmcnt<kLoads>(); else layer_wait_vmcnt<0>();
+    barrier();
+    if (c + 2 < nch) issue(c + 2, slot == 0 ? 2 : slot - 1);
+    compute(slot);
+    slot = slot == kXRing - 1 ? 0 : slot + 1;
+  }
+  // sum the k-groups: groups 1.. park theirs in the (now idle) ring
+  barrier();
+  f32x4 *red = reinterpret_cast<f32x4 *>(ring);
+  if (kg > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[((kg - 1) * NJ + jt) * 256 + (16 * i + r) * 4 + gq] = acc[i];
+  }
+  barrier();
+  if (kg == 0) {
+#pragma unroll 1
+    for (int q = 1; q < KG; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += red[((q - 1) * NJ + jt) * 256 + (16 * i + r) * 4 + gq];
+  }
+  f32x4 acc1[4];  // with RoPE: the partner tile, from wavefront 1
+  if constexpr (kRope) {
+    barrier();
+    if (w == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(16 * i + r) * 4 + gq] = acc[i];
+    }
+    barrier();
+    if (w == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc1[i] = red[(16 * i + r) * 4 + gq];
+    }
+  }
+  if (w != 0) return;
+
+  uint16_t *dst = g.y;
+  int64_t row_stride = g.N, col0 = f0;
+  bool rotate = false;
+  double f[4];
+  if (kRope) {
+    const int head = f0 / kHead;
+    int H, hh;
+    if (head < g.Hq) {
+      dst = g.q; H = g.Hq; hh = head;
+    } else if (head < g.Hq + g.Hkv) {
+      dst = g.k; H = g.Hkv; hh = head - g.Hq;
+    } else {
+      dst = g.v; H = g.Hkv; hh = head - g.Hq - g.Hkv;
+    }
+    row_stride = (int64_t)H * kHead;
+    col0 = (int64_t)hh * kHead + (f0 % kHead);
+    rotate = head < g.Hq + g.Hkv;
+    if (rotate) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = rope_turns_per_pos(16 * (b & 3) + 4 * gq + e, g.rope_log2_step);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 16 * i + r;
+    if (m >= g.M) continue;
+    uint16_t *dr = dst + (int64_t)m * row_stride + col0 + 4 * gq;
+    f32x4 o0 = acc[i];
+    if constexpr (kRope) {
+      f32x4 o1 = acc1[i];
+      if (rotate) {
+        const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float c, sn;
+          rope_cos_sin(p, f[e], c, sn);
+          o0[e] = acc[i][e] * c - acc1[i][e] * sn;
+          o1[e] = acc1[i][e] * c + acc[i][e] * sn;
+        }
+      }
+      *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+    }
+    *reinterpret_cast<u32x2 *>(dr) = u32x2{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
+  }
+}
+
+template <bool kRope>
+__global__ __launch_bounds__(512) void linear_skinny_lds_kernel(LinearArgs g) {
+  skinny_lds_product<kRope>(g);
+}
+
 inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s); }
 
 int launch_linear(LinearArgs g, bool rope, pkv_stream_t stream) {
+  if (g.M <= kSkinnyRows && g.K % kXChunk == 0) {
+    if (rope)
+      hipLaunchKernelGGL((linear_skinny_lds_kernel<true>), dim3((unsigned)(g.N / 32)), dim3(512), 0,
+                         as_stream(stream), g);
+    else
+      hipLaunchKernelGGL((linear_skinny_lds_kernel<false>), dim3((unsigned)(g.N / 16)), dim3(512), 0,
+                         as_stream(stream), g);
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_EHIP;
+  }
   if (g.M <= kSkinnyRows && g.K % 128 == 0) {
     if (rope) {
       hipLaunchKernelGGL((linear_skinny_kernel<true, 4>), dim3((unsigned)(g.N / 32)), dim3(256), 0,
