@@ -59,7 +59,11 @@ def _close(got_bits, ref, label):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (64, 384, 4096), (5, 4096, 4096), (65, 256, 256), (300, 384, 512),
-                                   (513, 128, 4096), (4096, 4096, 64), (4000, 4224, 128)])
+                                   (513, 128, 4096), (4096, 4096, 64), (4000, 4224, 128),
+                                   # few rows, inner dimension a multiple of 256: rows and weights staged
+                                   # through LDS (one chunk, two chunks, an odd count, rows not a
+                                   # multiple of 16)
+                                   (1, 128, 256), (33, 256, 512), (17, 128, 768), (63, 512, 1280)])
 def test_linear_matches_oracle(dev, M, N, K):
     rng = np.random.default_rng(M * 7 + N + K)
     x, w = _bf16(rng, (M, K)), _bf16(rng, (N, K), 1.0 / np.sqrt(K))
@@ -84,9 +88,10 @@ def test_linear_rejects_unsupported_shapes(dev):
     ("chunks-and-decode", [(30720, 70), (0, 33), (5000, 1), (4095, 1), (1, 2)]),
     ("long-prefill", [(0, 1500), (100, 547), (9000, 1)]),
     ("decode-h384", [(5000, 1), (10, 1), (0, 3), (77, 1)]),   # few rows, hidden 384: four-wavefront form
+    ("decode-h1024", [(3000, 1), (5, 1), (0, 2), (31000, 1)]),  # few rows, hidden 1024: LDS-staged form
 ])
 def test_qkv_rope_matches_oracle(dev, name, seqs):
-    hidden, Hq, Hkv = {"long-prefill": 64, "decode-h384": 384}.get(name, 512), 32, 8
+    hidden, Hq, Hkv = {"long-prefill": 64, "decode-h384": 384, "decode-h1024": 1024}.get(name, 512), 32, 8
     cu = np.concatenate([[0], np.cumsum([n for _, n in seqs])]).astype(np.int32)
     sl = np.array([c + n for c, n in seqs], dtype=np.int32)
     T = int(cu[-1])
