@@ -574,6 +574,324 @@ __device__ __forceinline__ Item load_item(const AttnArgs &a, int idx) {
 }
 
 // ---------------------------------------------------------------------------
+// Narrow wavefront stream.  A narrow wavefront's items (consecutive segments
+// of the concatenated (tile, kv head) key streams) are walked as ONE stream
+// of 32-key chunks: the chunk after the current one is always in flight,
+// also when it belongs to the next item, so an item boundary costs no load
+// latency.  Each chunk carries the Q^T operand of its item (4 KiB, reread
+// from cache per chunk), so nothing of an item is held across the boundary
+// but its accumulator.
+//
+// Finished items' outputs are not stored as they finish: they are parked in
+// the wavefront's 16 KiB of LDS (64 records of 256 bytes, a bf16 output
+// column per record, an fp32 partial column in two) and written out when the
+// records run out and at the end of the stream.  The vector memory counter
+// retires loads and stores in issue order, and a store takes long to retire
+// under a full read stream, so every store issued between the chunk loads
+// held up the next chunk's wait (measured on MI355X: eight stores per item
+// cost about one chunk time per item, a tenth of a step at 16 items per
+// wavefront).  Record j's destination lives in lane j's registers.
+// ---------------------------------------------------------------------------
+constexpr int kStashRecs = 64;     // records per wavefront (one per lane)
+constexpr int kStashRecVec = 16;   // u32x4 per record (256 bytes)
+constexpr int kStashVec = kStashRecs * kStashRecVec;  // u32x4 per wavefront (16 KiB)
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+struct StreamChunk {
+  u32x4 q[4];  // Q^T operand of the chunk's item: dims 32c + 8g .. +7 of column r
+  u32x4 k[8];
+  u32x4 v[8];
+  Item it;     // the chunk's item (wave-uniform)
+  int cc;      // chunk index within the item
+  bool last;   // last chunk of the item
+  bool bad0, bad1;
+};
+
+__device__ __forceinline__ int item_chunks(const Item &it) { return it.k1 > it.k0 ? (it.k1 - it.k0 + 31) >> 5 : 0; }
+
+
+__device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1, lds_u32x4 *stash) {
+  if (i0 >= i1) return;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int r = lane & 15;
+  const int log2G = a.log2G;
+  const int G = 1 << log2G;
+  const int Hq = a.Hq;
+  const int pc = r >> log2G;  // position (within the tile) of this lane's column r
+  const int ho = r & (G - 1);  // query head (within the group) of column r
+
+  // ---- chunks of the whole stream: every item's count, summed over the wave
+  int total = 0;
+  for (int b = i0; b < i1; b += 64) {
+    int n = 0;
+    if (b + lane < i1) {
+      const Item *p = a.items + b + lane;
+      n = p->k1 > p->k0 ? (p->k1 - p->k0 + 31) >> 5 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    total += __builtin_amdgcn_readfirstlane(n);
+  }
+  if (total == 0) return;
+
+  // per-lane constant parts of the K/V operand addresses (as in run_item)
+  const int ka = r >> 2, kbb = r & 3;
+  const int k_sel = ka >> 1;
+  const int k_row_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g;
+  const int v_sel = g >> 1;
+  const int v_off = r * pkv::kBlock + 8 * (g & 1);
+  const int64_t blk_stride = (int64_t)a.Hkv * TILE;
+
+  // ---- load cursor (wave-uniform): item li (fields itL, nchL chunks), its
+  // chunk lc, the block ids of that chunk's two blocks, and the next item's
+  // fields, fetched one item ahead
+  int li = i0, lc = 0;
+  Item itL = load_item(a, li), itN = itL;
+  int nchL = item_chunks(itL);
+  while (nchL == 0 && ++li < i1) {
+    itL = load_item(a, li);
+    nchL = item_chunks(itL);
+  }
+  if (li + 1 < i1) itN = load_item(a, li + 1);
+  auto block_id = [&](const Item &it, int j) -> int {
+    const int lb = (it.k0 >> 4) + j;
+    const int kb_end = min((it.k1 + 15) >> 4, a.bt_stride);
+    return lb < kb_end ? sload(a.bt + (int64_t)it.seq * a.bt_stride, lb) : -1;
+  };
+  int nb0 = block_id(itL, 0), nb1 = block_id(itL, 1);
+
+  // move the cursor one chunk on; block ids of the new position are fetched
+  // here, a chunk before they are needed
+  auto advance = [&]() {
+    if (++lc == nchL) {
+      lc = 0;
+      do {
+        if (++li >= i1) break;
+        itL = itN;
+        if (li + 1 < i1) itN = load_item(a, li + 1);
+        nchL = item_chunks(itL);
+      } while (nchL == 0);
+    }
+    if (li < i1) {
+      nb0 = block_id(itL, 2 * lc);
+      nb1 = block_id(itL, 2 * lc + 1);
+    }
+  };
+
+  // Issue the 20 loads of the cursor's chunk (4 of Q, 8 of K, 8 of V).  The
+  // same loads on every path, so each wait leaves the next chunk in flight.
+  auto issue = [&](StreamChunk &ch) {
+    const Item &it = itL;
+    ch.it = it;
+    ch.cc = lc;
+    ch.last = lc + 1 == nchL;
+    const int key0 = it.k0 + 32 * lc;
+    const bool need1 = key0 + 16 < it.k1;
+    const bool ok0 = nb0 >= 0 && nb0 < a.num_blocks;
+    const bool ok1 = nb1 >= 0 && nb1 < a.num_blocks;
+    const int64_t head_off = (int64_t)it.kvh * TILE;
+    const int64_t t0 = (ok0 ? (int64_t)nb0 * blk_stride : 0) + head_off;
+    const int64_t t1 = need1 && ok1 ? (int64_t)nb1 * blk_stride + head_off : t0;
+    // columns past the tile read the zero tile
+    const uint16_t *qp = pc < it.np ? a.q + ((int64_t)(it.t0 + pc) * Hq + it.kvh * G + ho) * D + 8 * g
+                                    : a.zero + 8 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ch.q[c] = load16(qp + 32 * c);
+    const uint16_t *kp = a.kc + (k_sel ? t1 : t0) + k_row_off;
+    const uint16_t *vp = a.vc + (v_sel ? t1 : t0) + v_off;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * kKGroup + c * kKGroupElems);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * pkv::kBlock);
+    ch.bad0 = !ok0;
+    ch.bad1 = need1 && !ok1;
+  };
+
+  f32x4 acc[8];
+  float m_run = neg_inf(), l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- parked outputs: records [0, nrec); lane j holds record j's
+  // destination: a row-head index (bf16 output, 256 bytes) or, where bit j
+  // of pmask is set, 2 * partial column + half (fp32, 2 x 256 bytes); where
+  // bit j of mlmask is set, also that partial column's (max, sum)
+  int nrec = 0;
+  uint64_t pmask = 0, mlmask = 0;
+  uint32_t rec_idx = 0;
+  float rec_m = 0.f, rec_l = 0.f;
+  auto flush = [&]() {
+    for (int q = 0; q < nrec; q += 4) {
+      const int j = q + (lane >> 4), piece = lane & 15;
+      const uint32_t idx = (uint32_t)__shfl((int)rec_idx, j);
+      if (j < nrec) {
+        const u32x4 d = stash[j * kStashRecVec + piece];
+        char *dst = (pmask >> j) & 1
+                        ? reinterpret_cast<char *>(a.part_o) + (int64_t)(idx >> 1) * (D * 4) + (idx & 1) * 256
+                        : reinterpret_cast<char *>(a.out) + (int64_t)idx * (D * 2);
+        *reinterpret_cast<u32x4 *>(dst + 16 * piece) = d;
+      }
+    }
+    if (lane < nrec && ((mlmask >> lane) & 1)) a.part_ml[rec_idx >> 1] = make_float2(rec_m, rec_l);
+    nrec = 0;
+    pmask = mlmask = 0;
+  };
+
+  auto finish = [&](const Item &it) {
+    const float l_tot = xsum32(xsum16(l_run));
+    const int ncols = min(it.np << log2G, 16);  // columns r < ncols hold a query
+    const bool part = it.part >= 0;
+    const int need = part ? 2 * ncols : ncols;
+    if (nrec + need > kStashRecs) flush();
+    const int jr = lane - nrec;  // this lane's record within the item
+    if (part) {
+      // fp32 partial of column r: records nrec + 2r (dims 0..63), nrec + 2r + 1
+      if (r < ncols) {
+        lds_u32x4 *rec = stash + (nrec + 2 * r) * kStashRecVec + g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) rec[4 * dt] = __builtin_bit_cast(u32x4, acc[dt]);
+      }
+      const int c = jr >> 1;
+      const float cm = __shfl(m_run, c), cl = __shfl(l_tot, c);
+      if (jr >= 0 && jr < need) {
+        rec_idx = (uint32_t)(2 * (it.part + c) + (jr & 1));
+        if ((jr & 1) == 0) {
+          rec_m = cm;
+          rec_l = cl;
+        }
+      }
+      const uint64_t bits = need == 64 ? ~0ull : ((1ull << need) - 1);
+      pmask |= bits << nrec;
+      mlmask |= (bits & 0x5555555555555555ull) << nrec;
+    } else {
+      if (r < ncols) {
+        const float inv = 1.f / l_tot;
+        lds_u32x2 *rec = reinterpret_cast<lds_u32x2 *>(stash + (nrec + r) * kStashRecVec) + g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const f32x4 v = acc[dt] * inv;
+          u32x2 w;
+          w[0] = pack_bf16(v[0], v[1]);
+          w[1] = pack_bf16(v[2], v[3]);
+          rec[4 * dt] = w;
+        }
+      }
+      if (jr >= 0 && jr < need)
+        rec_idx = (uint32_t)((it.t0 + (jr >> log2G)) * Hq + it.kvh * G + (jr & (G - 1)));
+    }
+    nrec += need;
+    m_run = neg_inf();
+    l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto compute = [&](StreamChunk &ch) {
+    const Item &it = ch.it;
+    const int key0 = it.k0 + 32 * ch.cc;
+    const int kl = key0 + 8 * g;  // key of this lane's slot 0
+    if (ch.bad0 || ch.bad1) {
+      // table entry outside [0, num_blocks): that block's keys and values are 0
+      const bool kz = k_sel ? ch.bad1 : ch.bad0;
+      const bool vz = v_sel ? ch.bad1 : ch.bad0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (kz) ch.k[i] = u32x4{0, 0, 0, 0};
+        if (vz) ch.v[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (key0 + 32 > it.k1) {
+      // keys past the range may hold stale data: zero their V
+      const int nv = it.k1 - kl;
+      u32x4 keep;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        keep[i] = (2 * i < nv ? 0x0000FFFFu : 0u) | (2 * i + 1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) ch.v[dt] &= keep;
+    }
+    const bool edge = key0 + 32 > it.k1 || key0 + 31 > it.pos0;
+    const int col_pos = it.pos0 + pc;
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s0 = mfma(ch.k[c], ch.q[c], s0);
+      s1 = mfma(ch.k[4 + c], ch.q[c], s1);
+    }
+    float sv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = s0[i];
+      sv[4 + i] = s1[i];
+    }
+    if (edge) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = kl + j;
+        sv[j] = key < it.k1 && key <= col_pos ? sv[j] : neg_inf();
+      }
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    // raw scores until here: the scale (> 0) commutes with the maximum
+    mx = xmax32(xmax16(mx)) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == neg_inf() ? 0.f : m_new;
+    float lsum = 0.f;
+    u32x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i], a.scale_log2, -m_use)),
+                                   __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * i + 1], a.scale_log2, -m_use)));
+      pb[i] = w;
+      lsum += bf16_lo(w) + bf16_hi(w);
+    }
+    // rescale only when some column's maximum moved (wave-uniform test)
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+    } else {
+      l_run += lsum;
+    }
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma(ch.v[dt], pb, acc[dt]);
+    if (ch.last) finish(it);
+  };
+
+  // ---- the stream: the next chunk's loads are issued before each chunk's
+  // math; the tail is peeled so the loop body always issues
+  StreamChunk A, B;
+  issue(A);
+  advance();
+  int sidx = 0;
+  for (; sidx + 2 < total; sidx += 2) {
+    issue(B);
+    advance();
+    compute(A);
+    issue(A);
+    advance();
+    compute(B);
+  }
+  if (sidx + 1 < total) {
+    issue(B);
+    advance();
+    compute(A);
+    compute(B);
+  } else {
+    compute(A);
+  }
+  flush();
+}
+
+// ---------------------------------------------------------------------------
 // Wide prefill tiles.  A tile covers one (sequence, kv head) and up to 256/G
 // query positions: 256 columns (positions x the group's query heads).  A
 // persistent workgroup of eight wavefronts walks a list of tiles;
@@ -1147,12 +1465,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(AttnArgs a) {
   const int w = blockIdx.x;
   if (w >= a.num_waves) return;
-  const int i0 = sload(a.waves, w);
-  const int i1 = sload(a.waves, w + 1);
-  for (int i = i0; i < i1; ++i) {
-    const Item it = load_item(a, i);
-    if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
-  }
+  __shared__ u32x4 stash[kStashVec];
+  narrow_stream(a, sload(a.waves, w), sload(a.waves, w + 1), (lds_u32x4 *)stash);
 }
 
 // Launch with wide tiles: a fixed grid of persistent workgroups in rows of
@@ -1167,20 +1481,17 @@ __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(A
   if (j >= a.num_wg) return;
   const pkv::RowRole role = pkv::mixed_row(a.num_wg / 8, a.narrow_rows, j / 8);
   if (role.narrow) {
-    // narrow wavefronts use no LDS and no barriers, so the wide loop below
-    // may start on some wavefronts while others still stream
     const int w = (role.ord * 8 + j % 8) * 8 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w < a.num_waves) {
-      const int i0 = a.num_wide + sload(a.waves, w);
-      const int i1 = a.num_wide + sload(a.waves, w + 1);
-      for (int i = i0; i < i1; ++i) {
-        const Item it = load_item(a, i);
-        if (it.k1 > it.k0 && it.np > 0) run_item<1>(a, it);
-      }
-    }
+    // each wavefront parks its finished outputs in its own 16 KiB of the
+    // chunk ring, which the wide loop below only fills after the barrier
+    static_assert(pkv::kWideWaves * kStashVec <= kNbuf * kChunkVec, "stashes fit in the ring");
+    if (w < a.num_waves)
+      narrow_stream(a, a.num_wide + sload(a.waves, w), a.num_wide + sload(a.waves, w + 1),
+                    (lds_u32x4 *)lds_chunks + (threadIdx.x >> 6) * kStashVec);
     // nothing of the narrow walk stays in flight: the wide loop's own waits
     // are then the only ones its tile loop needs
     wait_vmcnt<0>();
+    __syncthreads();
   }
   const int i0 = sload(a.wg_list, j);
   const int i1 = sload(a.wg_list, j + 1);
