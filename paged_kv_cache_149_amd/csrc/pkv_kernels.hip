@@ -1412,19 +1412,28 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       }
     }
 
-    // epilogue: O / l
+    // epilogue: O / l.  Lane (r, g) holds dims 16 dt + 4 g .. +3 of column
+    // r; one v_permlane16_swap per dword pair of chunks dt = 2k, 2k + 1
+    // hands it 8 consecutive dims instead (g = 0: 32k + 0..7, g = 2:
+    // 32k + 8.., g = 1: 32k + 16.., g = 3: 32k + 24..), so each 16-byte
+    // store covers 64 contiguous bytes of a column across its four lanes:
+    // half the line pieces of 8-byte stores, which cost the CU's memory
+    // pipeline far more than their bytes.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      if (!col_ok[nt]) continue;
       const float inv = 1.f / l_tot[nt];
-      uint16_t *op = a.out + col_qoff[nt] + 4 * g;
+      const int col = nt * 16 + r;
+      const int pc = col >> a.log2G;
+      uint16_t *const op =
+          a.out + ((int64_t)(d.t0 + w * WP + pc) * a.Hq + d.kvh * G + (col & (G - 1))) * D + 16 * (g & 1) + 8 * (g >> 1);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 v = acc[nt][dt] * inv;
-        u32x2 o;
-        o[0] = pack_bf16(v[0], v[1]);
-        o[1] = pack_bf16(v[2], v[3]);
-        *reinterpret_cast<u32x2 *>(op + 16 * dt) = o;
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 v0 = acc[nt][2 * k] * inv, v1 = acc[nt][2 * k + 1] * inv;
+        uint32_t x0 = pack_bf16(v0[0], v0[1]), x1 = pack_bf16(v0[2], v0[3]);
+        uint32_t y0 = pack_bf16(v1[0], v1[1]), y1 = pack_bf16(v1[2], v1[3]);
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
+                     : "+v"(x0), "+v"(y0), "+v"(x1), "+v"(y1));
+        if (pc < wnp) *reinterpret_cast<u32x4 *>(op + 32 * k) = u32x4{x0, x1, y0, y1};
       }
     }
     g_base += d.nch;
