@@ -896,7 +896,8 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
 // query positions: 256 columns (positions x the group's query heads).  A
 // persistent workgroup of eight wavefronts walks a list of tiles;
 // wavefront w owns columns [32w, 32w + 32) of each, two wavefronts per
-// SIMD, so one's softmax overlaps the other's matrix work.  Keys and values
+// SIMD, one's softmax issued beside the other's matrix work (on gfx950 the
+// two still take about the sum of their times).  Keys and values
 // stream in 32-key chunks (16 KiB), each staged once per workgroup in LDS by
 // direct global->LDS loads, laid out in MFMA operand order: region R (1 KiB)
 // holds, at byte 16*l, the 16 bytes lane l needs -- K operand (m-tile R/4,
