@@ -98,6 +98,47 @@ __device__ inline int row_position(const int32_t *__restrict__ cu, const int32_t
   return seq_lens[s] - (cu[s + 1] - cu[s]) + (t - cu[s]);
 }
 
+// Row positions for few-row kernels without a chain of dependent global
+// loads at the end: each lane of one wavefront loads entries lane and
+// lane + 64 of cu_seqlens and seq_lens when the kernel starts (their latency
+// hides behind the kernel's main loop); before the epilogue they go to LDS
+// and each row's sequence is found there.  Holds the tables of up to
+// kPosSeqs sequences; more fall back to row_position.
+constexpr int kPosSeqs = 127;
+struct RowTables {
+  int32_t cu0, cu1, sl0, sl1;  // this lane's entries lane and lane + 64 (clamped)
+};
+__device__ inline RowTables row_tables_load(const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
+                                            int S, int lane) {
+  RowTables t;
+  if (S >= 1 && S <= kPosSeqs) {
+    t.cu0 = cu[min(lane, S)];
+    t.cu1 = cu[min(lane + 64, S)];
+    t.sl0 = seq_lens[min(lane, S - 1)];
+    t.sl1 = seq_lens[min(lane + 64, S - 1)];
+  } else {
+    t.cu0 = t.cu1 = t.sl0 = t.sl1 = 0;
+  }
+  return t;
+}
+// lcu, lsl: 128 entries each in LDS, written here by the calling wavefront
+// (entries past S are clamped copies); then row t's position
+__device__ inline void row_tables_store(const RowTables &t, int32_t *lcu, int32_t *lsl, int lane) {
+  lcu[lane] = t.cu0;
+  lcu[lane + 64] = t.cu1;
+  lsl[lane] = t.sl0;
+  lsl[lane + 64] = t.sl1;
+}
+__device__ inline int row_position_lds(const int32_t *lcu, const int32_t *lsl, int S, int t) {
+  int lo = 0, hi = S;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (lcu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo < S ? lo : S - 1;
+  return lsl[s] - (lcu[s + 1] - lcu[s]) + (t - lcu[s]);
+}
+
 // Turns per position of pair i: theta^(-2i/128) / (2 pi) = 2^(-i * step) /
 // (2 pi), in double: at position p ~ 3e4 the angle is ~5e3 turns, and a
 // float's 2^-24 relative error there would already move it by ~2e-3 rad.
@@ -493,6 +534,10 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the rows' sequence tables, for RoPE's positions (wavefront 0)
+  __shared__ int32_t pos_cu[128], pos_sl[128];
+  RowTables rtab{};
+  if (kRope && w == 0) rtab = row_tables_load(g.cu, g.seq_lens, g.S, lane);
   auto compute = [&](int slot) {
     const uint32_t off = (uint32_t)(slot * kSlotVec * 16);
     u32x4 xb[SPW][4], wv[SPW];
@@ -524,7 +569,8 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
   // Chunk c is copied into slot c % 3 two chunks ahead, after the barrier
   // that follows everyone's reads of chunk c - 1 (the slot's previous
   // chunk).  Loads complete in order: at chunk c only chunk c + 1's
-  // kLoads loads may still fly behind it.
+  // kLoads loads may still fly behind it.  (Weights further ahead than the
+  // rows, in a ring of their own, measured no faster.)
   issue(0, 0);
   if (nch > 1) issue(1, 1);
   int slot = 0;
@@ -536,40 +582,32 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
     compute(slot);
     slot = slot == kXRing - 1 ? 0 : slot + 1;
   }
-  // sum the k-groups: groups 1.. park theirs in the (now idle) ring
+  // sum the k-groups and finish: every wavefront parks its partial sums in
+  // the (now idle) ring, then wavefront i (i < 4) adds up row tile i of
+  // both feature tiles and rotates and stores it, so the epilogue's work is
+  // spread over four wavefronts
   barrier();
   f32x4 *red = reinterpret_cast<f32x4 *>(ring);
-  if (kg > 0) {
+  auto red_at = [&](int grp, int tile, int i) -> f32x4 & { return red[((grp * NJ + tile) * 4 + i) * 64 + lane]; };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((kg - 1) * NJ + jt) * 256 + (16 * i + r) * 4 + gq] = acc[i];
-  }
+  for (int i = 0; i < 4; ++i) red_at(kg, jt, i) = acc[i];
+  if (kRope && w == 0 && g.S >= 1 && g.S <= kPosSeqs) row_tables_store(rtab, pos_cu, pos_sl, lane);
   barrier();
-  if (kg == 0) {
-#pragma unroll 1
-    for (int q = 1; q < KG; ++q)
+  if (w >= 4) return;
+  const int i = w;  // this wavefront's row tile
+  const int m = 16 * i + r;
+  f32x4 o0 = red_at(0, 0, i), o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kRope) o1 = red_at(0, 1, i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += red[((q - 1) * NJ + jt) * 256 + (16 * i + r) * 4 + gq];
+  for (int q = 1; q < KG; ++q) {
+    o0 += red_at(q, 0, i);
+    if constexpr (kRope) o1 += red_at(q, 1, i);
   }
-  f32x4 acc1[4];  // with RoPE: the partner tile, from wavefront 1
-  if constexpr (kRope) {
-    barrier();
-    if (w == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[(16 * i + r) * 4 + gq] = acc[i];
-    }
-    barrier();
-    if (w == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc1[i] = red[(16 * i + r) * 4 + gq];
-    }
-  }
-  if (w != 0) return;
+  if (m >= g.M) return;
 
   uint16_t *dst = g.y;
   int64_t row_stride = g.N, col0 = f0;
-  bool rotate = false;
-  double f[4];
-  if (kRope) {
+  if constexpr (kRope) {
     const int head = f0 / kHead;
     int H, hh;
     if (head < g.Hq) {
@@ -581,34 +619,23 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
     }
     row_stride = (int64_t)H * kHead;
     col0 = (int64_t)hh * kHead + (f0 % kHead);
-    rotate = head < g.Hq + g.Hkv;
-    if (rotate) {
+    if (head < g.Hq + g.Hkv) {  // queries and keys are rotated, values not
+      const bool lds_pos = g.S >= 1 && g.S <= kPosSeqs;
+      const double p = (double)(lds_pos ? row_position_lds(pos_cu, pos_sl, g.S, m)
+                                        : row_position(g.cu, g.seq_lens, g.S, m));
+      const f32x4 a0 = o0, a1 = o1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] = rope_turns_per_pos(16 * (b & 3) + 4 * gq + e, g.rope_log2_step);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = 16 * i + r;
-    if (m >= g.M) continue;
-    uint16_t *dr = dst + (int64_t)m * row_stride + col0 + 4 * gq;
-    f32x4 o0 = acc[i];
-    if constexpr (kRope) {
-      f32x4 o1 = acc1[i];
-      if (rotate) {
-        const double p = (double)row_position(g.cu, g.seq_lens, g.S, m);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float c, sn;
-          rope_cos_sin(p, f[e], c, sn);
-          o0[e] = acc[i][e] * c - acc1[i][e] * sn;
-          o1[e] = acc1[i][e] * c + acc[i][e] * sn;
-        }
+      for (int e = 0; e < 4; ++e) {
+        float c, sn;
+        rope_cos_sin(p, rope_turns_per_pos(16 * (b & 3) + 4 * gq + e, g.rope_log2_step), c, sn);
+        o0[e] = a0[e] * c - a1[e] * sn;
+        o1[e] = a1[e] * c + a0[e] * sn;
       }
-      *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
     }
-    *reinterpret_cast<u32x2 *>(dr) = u32x2{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
   }
+  uint16_t *dr = dst + (int64_t)m * row_stride + col0 + 4 * gq;
+  if constexpr (kRope) *reinterpret_cast<u32x2 *>(dr + 64) = u32x2{pack_bf16(o1[0], o1[1]), pack_bf16(o1[2], o1[3])};
+  *reinterpret_cast<u32x2 *>(dr) = u32x2{pack_bf16(o0[0], o0[1]), pack_bf16(o0[2], o0[3])};
 }
 
 template <bool kRope>
