@@ -458,15 +458,16 @@ __global__ __launch_bounds__(64 * kWaves) void linear_skinny_kernel(LinearArgs g
 // rate, about half of what 1 KiB contiguous loads reach.  Here the
 // workgroup copies each 256-deep chunk of the rows (64 rows x 512 bytes)
 // into an LDS ring by direct global->LDS loads of 1 KiB contiguous each (two
-// rows), and the weights of the chunk beside them in MFMA operand order (a
-// 1 KiB region per feature tile and 32-deep step); the wavefronts read
-// their operands from there.  A row's 16-byte pieces are stored
-// XOR-swizzled by the row's low four bits, so the 16 rows of one operand
-// read fall on distinct banks.  Wavefront w takes feature tile w % NJ and
-// 32-deep steps of each chunk by k-group w / NJ, and the k-groups' sums meet
-// in LDS.  The ring holds three chunks: the one being read, and two in
-// flight.  At 64 rows and hidden 4096 on MI355X: QKV with RoPE 35.6 -> 27.2
-// us, the output projection 25.3 -> 18.5 us against the form above.
+// rows), and the chunk's weight rows (16 per feature tile) beside them the
+// same way; the wavefronts read their operands from there.  A row's 16-byte
+// pieces are stored XOR-swizzled by the row's low four bits, so the 16 rows
+// of one operand read fall on distinct banks.  Wavefront w takes feature
+// tile w % NJ and 32-deep steps of each chunk by k-group w / NJ; the
+// k-groups' sums meet in LDS, and four wavefronts finish a row tile each.
+// The ring holds three chunks: the one being read, and two in flight.  At
+// 64 rows and hidden 4096 on MI355X: QKV with RoPE 35.6 -> 27.2 us, the
+// output projection 25.3 -> 18.5 us against the form above (before the
+// whole-row weight copies and the shared epilogue).
 constexpr int kXChunk = 256;                  // inner dimension per staged chunk
 constexpr int kXChunkVec = 64 * kXChunk / 8;  // u32x4 of a chunk's rows (32 KiB)
 constexpr int kXRing = 3;                     // chunk buffers
@@ -495,9 +496,11 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
 
   // this wavefront's copies of a chunk: rows 8w + 2q and 8w + 2q + 1 (q < 4),
   // lane l taking piece (l % 32) ^ (row % 16) of row 8w + 2q + l / 32 (rows
-  // past M read row M - 1: never stored); weight regions (tile, step) =
-  // (e / 8, e % 8) for e = NJ w + q (q < NJ), lane (r, gq) taking the
-  // 16 bytes at dimension 32 step + 8 gq of feature f0 + 64 tile + r
+  // past M read row M - 1: never stored); the weights the same way, 16
+  // feature rows per tile: copy e = NJ w + q (q < NJ) takes feature rows
+  // 2 (e % 8) and 2 (e % 8) + 1 of tile e / 8 (features f0 + 64 tile + row),
+  // so every copy reads whole 512-byte row pieces (64-byte pieces of 16
+  // rows cost ~10% more)
   const uint16_t *xsrc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -508,7 +511,8 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
 #pragma unroll
   for (int q = 0; q < NJ; ++q) {
     const int e = NJ * w + q;
-    wsrc[q] = g.w + (int64_t)(f0 + 64 * (e >> 3) + r) * g.K + 32 * (e & 7) + 8 * gq;
+    const int row = 2 * (e & 7) + (lane >> 5);
+    wsrc[q] = g.w + (int64_t)(f0 + 64 * (e >> 3) + row) * g.K + 8 * ((lane & 31) ^ row);
   }
   auto issue = [&](int c, int slot) {
     u32x4 *base = ring + slot * kSlotVec;
@@ -520,16 +524,16 @@ __device__ __forceinline__ void skinny_lds_product(const LinearArgs &g) {
       __builtin_amdgcn_global_load_lds(wsrc[q] + kXChunk * c, (lds_void_t *)(base + kXChunkVec + (NJ * w + q) * 64),
                                        16, 0, 0);
   };
-  // LDS byte addresses (slot 0) of this lane's operands of step t: the rows'
-  // piece 4 st + gq of row r (row tile 0) stored at (4 st + gq) ^ r, the
-  // weights' region (jt, st)
+  // LDS byte addresses (slot 0) of this lane's operands of step t: piece
+  // 4 st + gq of row r (row tile 0), and of feature row r of tile jt, each
+  // stored at (4 st + gq) ^ r
   uint32_t xaddr[SPW], waddr[SPW];
 #pragma unroll
   for (int t = 0; t < SPW; ++t) {
     const int st = kg * SPW + t;
     const __attribute__((address_space(3))) u32x4 *lds = (const __attribute__((address_space(3))) u32x4 *)ring;
     xaddr[t] = (uint32_t)(uintptr_t)(lds + r * 32 + ((4 * st + gq) ^ r));
-    waddr[t] = (uint32_t)(uintptr_t)(lds + kXChunkVec + (8 * jt + st) * 64 + lane);
+    waddr[t] = (uint32_t)(uintptr_t)(lds + kXChunkVec + jt * 512 + r * 32 + ((4 * st + gq) ^ r));
   }
   f32x4 acc[4];
 #pragma unroll
