@@ -1562,14 +1562,29 @@ __global__ __launch_bounds__(256) void swap_kernel(uint16_t *kc, uint16_t *vc, c
 }
 
 // ---------------------------------------------------------------------------
-// merge of key-split partials: one wavefront per (row, head); lane l owns
-// dimensions 2l, 2l+1
+// merge of key-split partials: one wavefront per (row, head), four per
+// workgroup.  Lane k first holds split k's (max, sum) -- 64 splits at a time
+// -- so the maximum and the normaliser are wave reductions of one load per
+// lane; then lane l owns dimensions 2l, 2l + 1 and adds the splits' partial
+// outputs with their weights (read across the lanes), four loads in flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void merge_kernel(const Merge *__restrict__ merges, int32_t n,
-                                                   const float2 *__restrict__ ml,
-                                                   const float *__restrict__ po,
-                                                   uint16_t *__restrict__ out) {
-  const int idx = blockIdx.x;
+constexpr int kMergeWaves = 4;
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Merge *__restrict__ merges, int32_t n,
+                                                                 const float2 *__restrict__ ml,
+                                                                 const float *__restrict__ po,
+                                                                 uint16_t *__restrict__ out) {
+  const int idx = blockIdx.x * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (idx >= n) return;
   const int lane = threadIdx.x & 63;
   const int32_t *e = reinterpret_cast<const int32_t *>(merges + idx);
@@ -1577,17 +1592,41 @@ __global__ __launch_bounds__(64) void merge_kernel(const Merge *__restrict__ mer
   const int first = __builtin_amdgcn_readfirstlane(e[1]);
   const int nsplit = __builtin_amdgcn_readfirstlane(e[2]);
   const int stride = __builtin_amdgcn_readfirstlane(e[3]);
+  // the maximum over all splits
   float M = neg_inf();
-  for (int k = 0; k < nsplit; ++k) M = fmaxf(M, ml[first + (int64_t)k * stride].x);
+  float2 mine = make_float2(neg_inf(), 0.f);  // this lane's split of the first 64
+  for (int k0 = 0; k0 < nsplit; k0 += 64) {
+    float2 v = make_float2(neg_inf(), 0.f);
+    if (k0 + lane < nsplit) v = ml[first + (int64_t)(k0 + lane) * stride];
+    if (k0 == 0) mine = v;
+    M = fmaxf(M, wave_max(v.x));
+  }
   float ax = 0.f, ay = 0.f, L = 0.f;
-  for (int k = 0; k < nsplit; ++k) {
-    const int64_t col = first + (int64_t)k * stride;
-    const float2 mlk = ml[col];
-    const float w = __builtin_amdgcn_exp2f(mlk.x - M);
-    const float2 o = *reinterpret_cast<const float2 *>(po + col * D + 2 * lane);
-    L += w * mlk.y;
-    ax += w * o.x;
-    ay += w * o.y;
+  for (int k0 = 0; k0 < nsplit; k0 += 64) {
+    float2 v = mine;
+    if (k0 > 0) v = k0 + lane < nsplit ? ml[first + (int64_t)(k0 + lane) * stride] : make_float2(neg_inf(), 0.f);
+    const float wk = k0 + lane < nsplit ? __builtin_amdgcn_exp2f(v.x - M) : 0.f;
+    L += wave_sum(wk * v.y);
+    const int nk = min(64, nsplit - k0);
+    int k = 0;
+    for (; k + 4 <= nk; k += 4) {
+      float2 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        o[u] = *reinterpret_cast<const float2 *>(po + ((int64_t)first + (int64_t)(k0 + k + u) * stride) * D + 2 * lane);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k + u));
+        ax += w * o[u].x;
+        ay += w * o[u].y;
+      }
+    }
+    for (; k < nk; ++k) {
+      const float2 o = *reinterpret_cast<const float2 *>(po + ((int64_t)first + (int64_t)(k0 + k) * stride) * D + 2 * lane);
+      const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wk), k));
+      ax += w * o.x;
+      ay += w * o.y;
+    }
   }
   const float inv = 1.f / L;
   reinterpret_cast<uint32_t *>(out + (int64_t)out_row * D)[lane] = pack_bf16(ax * inv, ay * inv);
@@ -1770,7 +1809,8 @@ int pkv_split_kv_reduce(const pkv_plan_t *plan, const void *ws, size_t ws_bytes,
   if (plan->num_merge == 0) return PKV_OK;
   if (!out) return PKV_EINVAL;
   const char *w = static_cast<const char *>(ws);
-  hipLaunchKernelGGL(merge_kernel, dim3(plan->num_merge), dim3(64), 0, as_stream(stream),
+  hipLaunchKernelGGL(merge_kernel, dim3((plan->num_merge + kMergeWaves - 1) / kMergeWaves), dim3(64 * kMergeWaves), 0,
+                     as_stream(stream),
                      reinterpret_cast<const Merge *>(w + plan->merge_off), plan->num_merge,
                      reinterpret_cast<const float2 *>(w + plan->ml_off),
                      reinterpret_cast<const float *>(w + plan->o_off), out);
