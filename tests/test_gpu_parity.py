@@ -267,6 +267,23 @@ def test_plan_options_same_result(dev, opts):
     check_attention(out, oracle.packed_attention(b), f"options {opts}")
 
 
+@pytest.mark.parametrize("narrow_waves", [8, 64, 1000])
+def test_narrow_stream_many_items(dev, narrow_waves):
+    """Decode rows and short prefill tails dealt to few wavefronts, so each
+    walks hundreds of items as one chunk stream: finished outputs (bf16 rows
+    and fp32 partials) overflow the wavefront's 64 parked records many times
+    and are written out mid-stream, and the items cut at share boundaries
+    write partials."""
+    rng = np.random.default_rng(71)
+    seqs = [(int(c), 1) for c in rng.integers(1, 300, size=500)]
+    seqs += [(int(c), int(n)) for c, n in zip(rng.integers(0, 200, size=12), rng.integers(2, 14, size=12))]
+    b = wl.make_batch("narrow-stream", seqs, seed=72)
+    note(f"narrow stream, {narrow_waves} wavefronts")
+    out, _, _, plan = run_step(b, dev, options={"narrow_waves": narrow_waves, "min_wave_keys": 32, "wide_tiles": 0})
+    assert plan.num_merge > 0
+    check_attention(out, oracle.packed_attention(b), f"narrow stream {narrow_waves}")
+
+
 @pytest.mark.parametrize("opts", [None, {"workgroups": 8}, {"workgroups": 16, "narrow_waves": 64}])
 def test_wide_lists_with_interior_chunks(dev, opts):
     """Prefill tiles long enough to have interior (unmasked) chunks beside
