@@ -743,7 +743,7 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
 
   auto finish = [&](const Item &it) {
     const float l_tot = xsum32(xsum16(l_run));
-    const int ncols = min(it.np << log2G, 16);  // columns r < ncols hold a query
+    const int ncols = max(0, min(it.np << log2G, 16));  // columns r < ncols hold a query
     const bool part = it.part >= 0;
     const int need = part ? 2 * ncols : ncols;
     if (nrec + need > kStashRecs) flush();
@@ -764,9 +764,11 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
           rec_l = cl;
         }
       }
-      const uint64_t bits = need == 64 ? ~0ull : ((1ull << need) - 1);
-      pmask |= bits << nrec;
-      mlmask |= (bits & 0x5555555555555555ull) << nrec;
+      if (need > 0) {  // need <= 32 and nrec + need <= 64 here
+        const uint64_t bits = ((1ull << need) - 1) << nrec;
+        pmask |= bits;
+        mlmask |= bits & (0x5555555555555555ull << nrec);
+      }
     } else {
       if (r < ncols) {
         const float inv = 1.f / l_tot;
