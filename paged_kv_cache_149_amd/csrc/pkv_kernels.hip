@@ -1158,19 +1158,17 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
           8 * g;
     }
   };
+  // (the addresses are formed here, from a descriptor fetched a tile
+  // earlier, so no tile start waits for its scalar loads)
   auto load_q = [&]() {
+    q_addresses(dn);
     q_load(qb, qnext);
     q_mark = n_issued;
   };
-  q_addresses(dn);
   load_q();
   for (int i = i0; i < i1; ++i) {
     const WideTile d = dn;
     const bool next_q = i + 1 < i1;
-    if (next_q) {
-      dn = wide_tile(a, i + 1);
-      q_addresses(dn);
-    }
     const int wpos0 = d.pos0 + w * WP;  // first position of this wavefront
     const int wnp = max(0, min(WP, d.np - w * WP));
     const int wlast = wpos0 + wnp - 1;
@@ -1351,6 +1349,9 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     wait_chunk(0);
     barrier();
     issue_next();
+    // the next tile's descriptor: issued beside the table entries that the
+    // next step's issue waits for anyway, so no wait covers only its latency
+    if (next_q) dn = wide_tile(a, i + 1);
     phase_v(-1, kAny);
     barrier();
     wait_q();
