@@ -319,6 +319,7 @@ struct AttnArgs {
   const int32_t *wg_list;  // launch with wide tiles: item offsets of each workgroup's list
   int32_t num_wg;        // launch with wide tiles: persistent workgroups
   int32_t narrow_rows;   // launch with wide tiles: rows of eight workgroups walking narrow shares first
+  int32_t nt_out;        // wide-tile outputs as non-temporal stores (the launch also streams decode items)
   int64_t num_blocks;
   int32_t bt_stride;
   int32_t num_items;
@@ -1416,8 +1417,12 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       }
     }
 
-    // epilogue: O / l.  Lane (r, g) holds dims 16 dt + 4 g .. +3 of column
-    // r; one v_permlane16_swap per dword pair of chunks dt = 2k, 2k + 1
+    // epilogue: O / l.  When the launch also streams decode items the
+    // stores are non-temporal: output lines written while HBM streams reads
+    // cost several times their bytes, and the hint took about 5% off a
+    // decode-heavy trace step; with prefill tiles alone it only cost time,
+    // so there the stores stay plain.  Lane (r, g) holds dims 16 dt + 4 g .. +3 of column r;
+    // one v_permlane16_swap per dword pair of chunks dt = 2k, 2k + 1
     // hands it 8 consecutive dims instead (g = 0: 32k + 0..7, g = 2:
     // 32k + 8.., g = 1: 32k + 16.., g = 3: 32k + 24..), so each 16-byte
     // store covers 64 contiguous bytes of a column across its four lanes:
@@ -1437,7 +1442,18 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
         uint32_t y0 = pack_bf16(v1[0], v1[1]), y1 = pack_bf16(v1[2], v1[3]);
         asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\ts_nop 1"
                      : "+v"(x0), "+v"(y0), "+v"(x1), "+v"(y1));
-        if (pc < wnp) *reinterpret_cast<u32x4 *>(op + 32 * k) = u32x4{x0, x1, y0, y1};
+        if (pc < wnp) {
+          u32x4 *dst = reinterpret_cast<u32x4 *>(op + 32 * k);
+          const u32x4 val = u32x4{x0, x1, y0, y1};
+          // In asm, since a non-temporal store beside a plain one is merged
+          // into one plain store.  The compiler's counted waits do not see
+          // it, which only makes them wait longer; the s_nop covers a VALU
+          // write to the data registers of a 16-byte store.
+          if (a.nt_out)
+            asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(dst), "v"(val) : "memory");
+          else
+            *dst = val;
+        }
       }
     }
     g_base += d.nch;
@@ -1780,6 +1796,7 @@ int pkv_varlen_attention_main(const pkv_bf16 *q, const pkv_bf16 *k_cache,
   a.wg_list = nullptr;
   a.num_wg = 0;
   a.narrow_rows = plan->narrow_rows;
+  a.nt_out = plan->num_waves > 0;
   a.num_blocks = num_blocks;
   a.bt_stride = bt_stride;
   a.num_items = plan->num_items;
