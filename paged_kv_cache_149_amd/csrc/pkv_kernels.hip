@@ -597,6 +597,7 @@ constexpr int kStashRecs = 64;     // records per wavefront (one per lane)
 constexpr int kStashRecVec = 16;   // u32x4 per record (256 bytes)
 constexpr int kStashVec = kStashRecs * kStashRecVec;  // u32x4 per wavefront (16 KiB)
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) int lds_int;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 struct StreamChunk {
@@ -612,7 +613,11 @@ struct StreamChunk {
 __device__ __forceinline__ int item_chunks(const Item &it) { return it.k1 > it.k0 ? (it.k1 - it.k0 + 31) >> 5 : 0; }
 
 
-__device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1, lds_u32x4 *stash) {
+// prog: the workgroup's eight progress words in LDS (zeroed before any
+// wavefront enters), slot: this wavefront's index in the workgroup; none for
+// one-wavefront workgroups.
+__device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1, lds_u32x4 *stash,
+                                              volatile lds_int *prog = nullptr, int slot = 0) {
   if (i0 >= i1) return;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
@@ -878,7 +883,21 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
   for (; sidx + 2 < total; sidx += 2) {
     issue(B);
     advance();
+    // Two wavefronts of a workgroup share each SIMD (slots s and s ^ 4).
+    // Left alone, the older one is served first and ends its equal share
+    // far earlier (on a decode-heavy trace step the younger ones ended 1.76x
+    // later); each posts its progress every two chunks and takes a higher
+    // priority while it trails its partner, so the pair ends together.
+    int other = 0;
+    if (prog) {
+      prog[slot] = sidx;
+      other = __builtin_amdgcn_readfirstlane(prog[slot ^ 4]);
+    }
     compute(A);
+    if (prog) {
+      if (sidx < other) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     issue(A);
     advance();
     compute(B);
@@ -1514,9 +1533,14 @@ __global__ __launch_bounds__(64 * pkv::kWideWaves) void attention_mixed_kernel(A
     // each wavefront parks its finished outputs in its own 16 KiB of the
     // chunk ring, which the wide loop below only fills after the barrier
     static_assert(pkv::kWideWaves * kStashVec <= kNbuf * kChunkVec, "stashes fit in the ring");
+    __shared__ int prog[8];
+    if ((threadIdx.x & 63) == 0) prog[threadIdx.x >> 6] = 0;
+    __syncthreads();
     if (w < a.num_waves)
       narrow_stream(a, a.num_wide + sload(a.waves, w), a.num_wide + sload(a.waves, w + 1),
-                    (lds_u32x4 *)lds_chunks + (threadIdx.x >> 6) * kStashVec);
+                    (lds_u32x4 *)lds_chunks + (threadIdx.x >> 6) * kStashVec, (volatile lds_int *)prog,
+                    threadIdx.x >> 6);
+    __builtin_amdgcn_s_setprio(0);
     // nothing of the narrow walk stays in flight: the wide loop's own waits
     // are then the only ones its tile loop needs
     wait_vmcnt<0>();

@@ -23,6 +23,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -41,13 +42,25 @@ constexpr int kDefaultWorkgroups = 256;    // one per CU on an MI355X
 constexpr int kXcds = 8;                   // consecutive workgroups go to the XCDs in turn
 
 // Cost model of the launch with wide tiles, in CU-microseconds (measured on
-// MI355X): a wide tile costs ~0.9 us per 32-key chunk plus ~2 us to start;
-// a narrow workgroup streams its 32-key chunks (16 KiB of K and V) at
-// ~30 GB/s per CU.  (0.9 measured 1-1.5% faster than 1.1 or 0.75 on mixed
-// and trace steps; a larger start cost or another narrow rate, no better.)
+// MI355X): a wide tile costs ~0.9 us per 32-key chunk plus ~2 us to start.
+// The narrow streams (32-key chunks of 16 KiB of K and V) move ~5 GB/s per
+// wavefront until their sum nears ~6.1 TB/s of HBM, and bend over smoothly
+// there (timed per workgroup on trace steps: 1088 wavefronts 5.5 TB/s, 1216
+// 5.8, 1344 6.1, 1664 6.1); a 12-norm of the two bounds follows that bend.
 constexpr double kWideChunkUs = 0.9;
 constexpr double kWideTileUs = 2.0;
-constexpr double kNarrowChunkUs = 16384.0 / 30.0e3;
+constexpr double kNarrowWaveBytesPerUs = 5.0e3;
+constexpr double kNarrowHbmBytesPerUs = 6.1e6;
+constexpr double kChunkBytes = 16384.0;
+
+// time of the narrow shares when W wavefronts (eight per workgroup) share
+// total_chunks
+double narrow_share_us(int64_t total_chunks, int64_t W) {
+  const double waves = (double)W * kNarrowWaveBytesPerUs;
+  const double rate = waves / std::pow(1.0 + std::pow(waves / kNarrowHbmBytesPerUs, 12.0), 1.0 / 12.0);
+  const double longest = (double)((total_chunks + W - 1) / W) * kChunkBytes / kNarrowWaveBytesPerUs;
+  return std::max(longest, (double)total_chunks * kChunkBytes / rate);
+}
 
 }  // namespace
 
@@ -144,8 +157,17 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   int narrow_rows = 0;
   int want_waves = kDefaultNarrowWaves;
   if (n_wide > 0 && total_chunks > 0) {
-    const double narrow_us = (double)total_chunks * kNarrowChunkUs;
-    narrow_rows = std::max(1, std::min(max_rows, (int)(max_rows * narrow_us / (narrow_us + wide_us) + 0.5)));
+    // the fewest rows with the least estimated launch time: the narrow rows
+    // take their wide tiles after their shares, the grid shares the rest
+    double best = 0;
+    for (int r = 1; r <= max_rows; ++r) {
+      const double share = narrow_share_us(total_chunks, 64 * (int64_t)r);
+      const double t = std::max(share, (wide_us + 8.0 * r * share) / (8.0 * max_rows));
+      if (r == 1 || t < best * (1.0 - 1e-6)) {
+        best = t;
+        narrow_rows = r;
+      }
+    }
     want_waves = 64 * narrow_rows;
   }
   if (opts && opts->narrow_waves > 0) want_waves = opts->narrow_waves;
@@ -166,7 +188,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     const int rows = std::min(max_rows, narrow_rows + (n_wide + kXcds - 1) / kXcds);
     n_wg = rows * kXcds;
     // starting load: the narrow share of a narrow workgroup (eight wavefronts)
-    const double share_us = W > 0 ? 8.0 * ((total_chunks + W - 1) / W) * kNarrowChunkUs : 0.0;
+    const double share_us = W > 0 ? narrow_share_us(total_chunks, W) : 0.0;
     std::vector<double> load(n_wg, 0.0);
     for (int j = 0; j < n_wg; ++j) {
       if (pkv::mixed_row(rows, narrow_rows, j / kXcds).narrow) load[j] = share_us;
