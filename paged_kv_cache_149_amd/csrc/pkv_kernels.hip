@@ -57,6 +57,7 @@ constexpr int TILE = pkv::kBlock * pkv::kHeadDim;  // elements of a (block, head
 // lines (one 32-dimension MFMA step of 16 keys is 1 KiB contiguous).
 constexpr int kKGroup = 32;
 constexpr int kKGroupElems = pkv::kBlock * kKGroup;
+constexpr int kXcdCount = 8;  // XCDs of an MI355X; consecutive workgroups go to them in turn
 
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -185,8 +186,17 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 // consecutive slots of up to 16 consecutive rows -- whole sectors inside any
 // prefill run, whatever its alignment; decode rows touch one slot of a block
 // each.
+// Placement and write policy, both for the launch that follows: runs of 16
+// consecutive row groups go to one XCD (the runs to the XCDs in turn), so
+// the two groups that share a block write it through one L2; and every K/V
+// store is non-temporal, so the step's lines leave the caches during the
+// append.  Plain stores left them to be written back a few at a time while
+// the attention launch streams the pools, and a write under a full read
+// stream costs several times its bytes (on the 200-iteration trace both
+// changes together made the attention launches ~8% faster).
 // ---------------------------------------------------------------------------
 constexpr int kAppendRows = 16;
+constexpr int kAppendRun = 16;  // consecutive row groups per XCD on large steps
 
 template <int kAppendHeads>
 __global__ __launch_bounds__(256) void append_kernel(
@@ -195,10 +205,17 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
     int64_t num_blocks, int64_t *__restrict__ slot_out, uint16_t *__restrict__ kc,
-    uint16_t *__restrict__ vc) {
+    uint16_t *__restrict__ vc, int32_t run) {
   __shared__ int64_t srow[kAppendRows];
   __shared__ uint32_t vrow[kAppendHeads][kAppendRows][D / 2 + 1];  // +1: rows start in different banks
-  const int t0 = blockIdx.x * kAppendRows;
+  // runs of `run` consecutive row groups on one XCD, the runs dealt to the
+  // XCDs in turn (workgroups go to the XCDs in turn; gridDim.x is a
+  // multiple of 8 runs): a block that two groups of a run share is written
+  // through one L2, whose partial lines then merge before they reach HBM
+  const int place = blockIdx.x / kXcdCount;  // this workgroup's place on its XCD
+  const int grp = ((place / run) * kXcdCount + blockIdx.x % kXcdCount) * run + place % run;
+  const int t0 = grp * kAppendRows;
+  if (t0 >= T) return;  // padding of the grid
   const int h0 = blockIdx.y * kAppendHeads;
   const int nh = min(kAppendHeads, Hkv - h0);
   const int tid = threadIdx.x;
@@ -275,7 +292,7 @@ __global__ __launch_bounds__(256) void append_kernel(
                      d0 % kKGroup;
 #pragma unroll
       for (int j = 0; j < kAppendHeads; ++j)
-        if (j < nh) *reinterpret_cast<u32x4 *>(kp + j * TILE) = xk[j];
+        if (j < nh) __builtin_nontemporal_store(xk[j], reinterpret_cast<u32x4 *>(kp + j * TILE));
     }
   }
   // V, dimension-major: lanes over (row pair, dimension), pairs fastest, so a
@@ -294,10 +311,10 @@ __global__ __launch_bounds__(256) void append_kernel(
     const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
     uint16_t *vh = vc + (int64_t)(h0 + j) * TILE + (int64_t)d * pkv::kBlock;
     if (pair) {
-      *reinterpret_cast<uint32_t *>(vh + (s0 >> 4) * Hkv * TILE + (s0 & 15)) = a0 | (a1 << 16);
+      __builtin_nontemporal_store(a0 | (a1 << 16), reinterpret_cast<uint32_t *>(vh + (s0 >> 4) * Hkv * TILE + (s0 & 15)));
     } else {
-      if (s0 >= 0) vh[(s0 >> 4) * Hkv * TILE + (s0 & 15)] = (uint16_t)a0;
-      if (s1 >= 0) vh[(s1 >> 4) * Hkv * TILE + (s1 & 15)] = (uint16_t)a1;
+      if (s0 >= 0) __builtin_nontemporal_store((uint16_t)a0, vh + (s0 >> 4) * Hkv * TILE + (s0 & 15));
+      if (s1 >= 0) __builtin_nontemporal_store((uint16_t)a1, vh + (s1 >> 4) * Hkv * TILE + (s1 & 15));
     }
   }
 }
@@ -1690,13 +1707,18 @@ inline bool valid_scale(float scale) { return scale > 0.f && scale <= FLT_MAX; }
 void launch_append(const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_in, const int32_t *cu,
                    const int32_t *seq_lens, const int32_t *bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
                    int64_t num_blocks, int64_t *slot_out, uint16_t *kc, uint16_t *vc, hipStream_t stream) {
-  const unsigned groups = (unsigned)((T + kAppendRows - 1) / kAppendRows);
-  if (groups >= 256) {
+  const unsigned real_groups = (unsigned)((T + kAppendRows - 1) / kAppendRows);
+  // runs of 16 groups per XCD once there are 8 runs; plain turns below (a
+  // grid padded to 128 groups would cost a 64-row decode step ~0.6 us)
+  const int run = real_groups >= (unsigned)(kXcdCount * kAppendRun) ? kAppendRun : 1;
+  const unsigned unit = kXcdCount * run;
+  const unsigned groups = (real_groups + unit - 1) / unit * unit;
+  if (real_groups >= 256) {
     hipLaunchKernelGGL(append_kernel<4>, dim3(groups, (Hkv + 3) / 4), dim3(256), 0, stream, k_new, v_new, slot_in, cu,
-                       seq_lens, bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc);
+                       seq_lens, bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run);
   } else {
     hipLaunchKernelGGL(append_kernel<1>, dim3(groups, Hkv), dim3(256), 0, stream, k_new, v_new, slot_in, cu, seq_lens,
-                       bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc);
+                       bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run);
   }
 }
 
