@@ -756,7 +756,13 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
         char *dst = (pmask >> j) & 1
                         ? reinterpret_cast<char *>(a.part_o) + (int64_t)(idx >> 1) * (D * 4) + (idx & 1) * 256
                         : reinterpret_cast<char *>(a.out) + (int64_t)idx * (D * 2);
-        *reinterpret_cast<u32x4 *>(dst + 16 * piece) = d;
+        // final outputs non-temporal (they would otherwise be written back
+        // under a later launch's read stream); partials stay cached for the
+        // merge that reads them next
+        if ((pmask >> j) & 1)
+          *reinterpret_cast<u32x4 *>(dst + 16 * piece) = d;
+        else
+          __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(dst + 16 * piece));
       }
     }
     if (lane < nrec && ((mlmask >> lane) & 1)) a.part_ml[rec_idx >> 1] = make_float2(rec_m, rec_l);
@@ -1689,7 +1695,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(const Merge *__
     }
   }
   const float inv = 1.f / L;
-  reinterpret_cast<uint32_t *>(out + (int64_t)out_row * D)[lane] = pack_bf16(ax * inv, ay * inv);
+  // non-temporal: the row is not read again by this step
+  __builtin_nontemporal_store(pack_bf16(ax * inv, ay * inv), reinterpret_cast<uint32_t *>(out + (int64_t)out_row * D) + lane);
 }
 
 inline hipStream_t as_stream(pkv_stream_t s) { return static_cast<hipStream_t>(s); }
