@@ -189,10 +189,15 @@ typedef struct pkv_plan {
   int64_t kv_keys;        /* sum over sequences of visible keys (accounting) */
   int64_t visible_pairs;  /* sum over rows of visible keys (accounting) */
   int32_t num_workgroups; /* workgroups of a launch with wide tiles (0 if none) */
-  int32_t reserved;
+  int32_t num_append_groups; /* row groups of the step's append */
   int64_t wg_off;         /* byte offset in ws of int32[num_workgroups + 1]:
                              workgroup j's wide tiles are items
                              [list[j], list[j + 1]) */
+  int64_t append_off;     /* byte offset in ws of int32[2 * num_append_groups]:
+                             group g is rows [list[2g], list[2g] + list[2g + 1])
+                             of the packed batch, at most 16; the groups cover
+                             every row once, in order, and the rows a sequence
+                             appends into one block lie in one group */
 } pkv_plan_t;
 
 int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
@@ -215,10 +220,9 @@ int pkv_plan(const int32_t *h_cu_seqlens_q, const int32_t *h_seq_lens,
  * results (running max, sum, unnormalised output) into ws; every other row
  * writes out directly.  Accumulation is fp32; probabilities are rounded to
  * bf16 for the P.V product and the normaliser sums those rounded values;
- * out is rounded to bf16 (nearest even).  When scale <= 1/sqrt(head_dim),
- * prefill tiles multiply q by scale * log2(e) once and round it to bf16
- * again before the products (one more rounding of q); above that scale
- * they, like decode items, apply the scale in fp32.  Block-table entries outside
+ * out is rounded to bf16 (nearest even).  q enters the products as stored:
+ * prefill tiles and decode items alike apply the scale in fp32, inside each
+ * exponent's argument.  Block-table entries outside
  * [0, num_blocks) read as zero keys/values.  scale must be positive and
  * finite (the kernels take maxima of raw scores and scale them afterwards,
  * which only a positive scale commutes with).  Errors: PKV_EINVAL (null
@@ -254,10 +258,13 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                                pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * The whole step on one stream: pkv_slot_append (slot_mapping, device
- * int64[T], is written), then pkv_paged_varlen_attention.  Attention reads the cache
- * after the append, so each row sees its own new key.  A scale that is not
- * positive and finite returns PKV_EINVAL before the append is launched.
+ * The whole step on one stream: the append of pkv_slot_append (slot_mapping,
+ * device int64[T], is written; the same kernel, run on the plan's row groups,
+ * so each block the step fills is written by one workgroup), then
+ * pkv_paged_varlen_attention.  Attention reads the cache after the append, so
+ * each row sees its own new key.  A scale that is not positive and finite,
+ * and a plan whose row groups do not fit its workspace, return PKV_EINVAL
+ * before the append is launched.
  * ------------------------------------------------------------------------- */
 int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new,
                    const pkv_bf16 *v_new, pkv_bf16 *k_cache,

@@ -54,8 +54,8 @@ class PlanStruct(ctypes.Structure):
                 ("zero_off", ctypes.c_int64),
                 ("ws_bytes", ctypes.c_size_t), ("host_bytes", ctypes.c_size_t),
                 ("kv_keys", ctypes.c_int64), ("visible_pairs", ctypes.c_int64),
-                ("num_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("wg_off", ctypes.c_int64)]
+                ("num_workgroups", ctypes.c_int32), ("num_append_groups", ctypes.c_int32),
+                ("wg_off", ctypes.c_int64), ("append_off", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -261,6 +261,13 @@ class Plan:
         n = self.st.num_workgroups + 1 if self.st.num_workgroups > 0 else 0
         off = self.st.wg_off
         return self.staging[off:off + n * 4].numpy().view(np.int32).copy()
+
+    def append_groups(self) -> np.ndarray:
+        """The append's row groups: [num_append_groups, 2] (first packed row,
+        row count)."""
+        n = self.st.num_append_groups
+        off = self.st.append_off
+        return self.staging[off:off + n * 8].numpy().view(np.int32).reshape(n, 2).copy()
 
     def merges(self) -> np.ndarray:
         n = self.st.num_merge

@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
     int64_t num_blocks, int64_t *__restrict__ slot_out, uint16_t *__restrict__ kc,
-    uint16_t *__restrict__ vc, int32_t run) {
+    uint16_t *__restrict__ vc, int32_t run, const int2 *__restrict__ groups, int32_t ngroups) {
   __shared__ int64_t srow[kAppendRows];
   __shared__ uint32_t vrow[kAppendHeads][kAppendRows][D / 2 + 1];  // +1: rows start in different banks
   // runs of `run` consecutive row groups on one XCD, the runs dealt to the
@@ -214,13 +214,23 @@ __global__ __launch_bounds__(256) void append_kernel(
   // through one L2, whose partial lines then merge before they reach HBM
   const int place = blockIdx.x / kXcdCount;  // this workgroup's place on its XCD
   const int grp = ((place / run) * kXcdCount + blockIdx.x % kXcdCount) * run + place % run;
-  const int t0 = grp * kAppendRows;
-  if (t0 >= T) return;  // padding of the grid
+  // rows t0 .. t0 + n - 1: the planner's group grp, else 16 rows from 16 grp
+  int t0, n;
+  if (groups) {
+    if (grp >= ngroups) return;  // padding of the grid
+    const int2 gd = groups[grp];
+    t0 = gd.x;
+    n = gd.y;
+  } else {
+    t0 = grp * kAppendRows;
+    if (t0 >= T) return;  // padding of the grid
+    n = min(kAppendRows, T - t0);
+  }
   const int h0 = blockIdx.y * kAppendHeads;
   const int nh = min(kAppendHeads, Hkv - h0);
   const int tid = threadIdx.x;
   const int ri = tid >> 4, d0 = 8 * (tid & 15);  // this thread's row and dimensions
-  const bool row_ok = t0 + ri < T;
+  const bool row_ok = ri < n;
   // the rows' K (kept in registers) and V (staged in LDS), before the slots
   u32x4 xk[kAppendHeads];
   if (row_ok) {
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     if (slot_in) {
       if (lane < kAppendRows) {
         int64_t sl = -1;
-        if (t0 + lane < T) {
+        if (lane < n) {
           sl = slot_in[t0 + lane];
           if (sl < 0 || sl >= num_blocks * pkv::kBlock) sl = -1;
         }
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(256) void append_kernel(
       if (lane < kAppendRows) {
         const int t = t0 + lane;
         int64_t sl = -1;
-        if (t < T) {
+        if (lane < n) {
           if (cnt < 64) {
             const int sq = min(s0 + cnt, S - 1);  // S - 1 unless the metadata is malformed
             const int c_lo = cnt == 0 ? cu_s0 : lo_e;
@@ -301,7 +311,7 @@ __global__ __launch_bounds__(256) void append_kernel(
   // consecutive, 4-byte-aligned slots is one 4-byte store
   const int p = tid & 7;  // this thread's row pair, the same in every round below
   const int r0 = 2 * p, r1 = r0 + 1;
-  const int64_t s0 = t0 + r0 < T ? srow[r0] : -1, s1 = t0 + r1 < T ? srow[r1] : -1;
+  const int64_t s0 = r0 < n ? srow[r0] : -1, s1 = r1 < n ? srow[r1] : -1;
   const bool pair = s0 >= 0 && s1 == s0 + 1 && (s0 & 1) == 0;
 #pragma unroll
   for (int k = 0; k < kAppendHeads * kAppendRows * D / 2 / 256; ++k) {
@@ -1713,8 +1723,10 @@ inline bool valid_scale(float scale) { return scale > 0.f && scale <= FLT_MAX; }
 // GPU (64 decode rows: 32 workgroups instead of 8).
 void launch_append(const uint16_t *k_new, const uint16_t *v_new, const int64_t *slot_in, const int32_t *cu,
                    const int32_t *seq_lens, const int32_t *bt, int32_t bt_stride, int32_t S, int32_t T, int32_t Hkv,
-                   int64_t num_blocks, int64_t *slot_out, uint16_t *kc, uint16_t *vc, hipStream_t stream) {
-  const unsigned real_groups = (unsigned)((T + kAppendRows - 1) / kAppendRows);
+                   int64_t num_blocks, int64_t *slot_out, uint16_t *kc, uint16_t *vc, hipStream_t stream,
+                   const int2 *plan_groups = nullptr, int32_t num_plan_groups = 0) {
+  const unsigned real_groups =
+      plan_groups ? (unsigned)num_plan_groups : (unsigned)((T + kAppendRows - 1) / kAppendRows);
   // runs of 16 groups per XCD once there are 8 runs; plain turns below (a
   // grid padded to 128 groups would cost a 64-row decode step ~0.6 us)
   const int run = real_groups >= (unsigned)(kXcdCount * kAppendRun) ? kAppendRun : 1;
@@ -1722,10 +1734,11 @@ void launch_append(const uint16_t *k_new, const uint16_t *v_new, const int64_t *
   const unsigned groups = (real_groups + unit - 1) / unit * unit;
   if (real_groups >= 256) {
     hipLaunchKernelGGL(append_kernel<4>, dim3(groups, (Hkv + 3) / 4), dim3(256), 0, stream, k_new, v_new, slot_in, cu,
-                       seq_lens, bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run);
+                       seq_lens, bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run, plan_groups,
+                       num_plan_groups);
   } else {
     hipLaunchKernelGGL(append_kernel<1>, dim3(groups, Hkv), dim3(256), 0, stream, k_new, v_new, slot_in, cu, seq_lens,
-                       bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run);
+                       bt, bt_stride, S, T, Hkv, num_blocks, slot_out, kc, vc, run, plan_groups, num_plan_groups);
   }
 }
 
@@ -1978,10 +1991,24 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
                    const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream) {
   if (!plan || !valid_scale(scale)) return PKV_EINVAL;
-  const int st = pkv_slot_append(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride,
-                                 plan->num_seqs, plan->num_rows, num_blocks, slot_mapping, k_cache,
-                                 v_cache, plan->num_kv_heads, plan->head_dim, stream);
-  if (st != PKV_OK) return st;
+  // pkv_slot_append's checks, then its kernel on the plan's row groups
+  const int32_t S = plan->num_seqs, T = plan->num_rows, Hkv = plan->num_kv_heads;
+  if (S < 0 || T < 0 || bt_stride < 0 || num_blocks < 0 || Hkv <= 0) return PKV_EINVAL;
+  if (plan->head_dim != D) return PKV_EUNSUPPORTED;
+  if (T > 0) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !cu_seqlens_q || !seq_lens || !block_tables ||
+        !slot_mapping || S == 0 || !ws)
+      return PKV_EINVAL;
+    const int32_t ng = plan->num_append_groups;
+    if (ng <= 0 || ng > T || plan->append_off < 0 || (size_t)plan->append_off + (size_t)ng * 8 > plan->ws_bytes)
+      return PKV_EINVAL;
+    if (ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
+    launch_append(k_new, v_new, nullptr, cu_seqlens_q, seq_lens, block_tables, bt_stride, S, T, Hkv, num_blocks,
+                  slot_mapping, k_cache, v_cache, as_stream(stream),
+                  reinterpret_cast<const int2 *>(static_cast<const char *>(ws) + plan->append_off), ng);
+    const int st = launch_status();
+    if (st != PKV_OK) return st;
+  }
   return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
                                     scale, plan, ws, ws_bytes, out, stream);
 }

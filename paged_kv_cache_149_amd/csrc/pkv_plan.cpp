@@ -130,6 +130,34 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     }
   }
 
+  // ---- the append's row groups (consecutive packed rows, at most 16): the
+  // rows a sequence appends into one block (a run) are never cut, so every
+  // block this step fills is written by one workgroup in whole lines;
+  // runs pack into groups in packed order (decode rows 16 to a group)
+  std::vector<int32_t> app;  // (first row, rows) pairs
+  {
+    int32_t g0 = 0, gn = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int ql = h_cu[s + 1] - h_cu[s];
+      const int c = h_seq_lens[s] - ql;
+      for (int j = 0; j < ql;) {
+        const int run = std::min(ql - j, pkv::kBlock - (c + j) % pkv::kBlock);
+        if (gn + run > pkv::kBlock) {
+          app.push_back(g0);
+          app.push_back(gn);
+          gn = 0;
+        }
+        if (gn == 0) g0 = h_cu[s] + j;
+        gn += run;
+        j += run;
+      }
+    }
+    if (gn > 0) {
+      app.push_back(g0);
+      app.push_back(gn);
+    }
+  }
+
   std::vector<Item> items;
   std::vector<Merge> merges;
   std::vector<int32_t> wave_off;
@@ -286,10 +314,12 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   plan->kv_keys = kv_keys;
   plan->visible_pairs = pairs;
   plan->num_workgroups = n_wg;
+  plan->num_append_groups = (int32_t)(app.size() / 2);
   const size_t items_b = pkv::align_up(items.size() * sizeof(Item));
   const size_t waves_b = pkv::align_up(wave_off.size() * sizeof(int32_t));
   const size_t merge_b = pkv::align_up(merges.size() * sizeof(Merge));
   const size_t wg_b = pkv::align_up(wg_list.size() * sizeof(int32_t));
+  const size_t app_b = pkv::align_up(app.size() * sizeof(int32_t));
   // a zero (block, head) tile: loads of table entries outside [0, num_blocks)
   // are pointed at it
   const size_t zero_b = (size_t)pkv::kBlock * pkv::kHeadDim * 2;
@@ -297,11 +327,12 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   plan->waves_off = (int64_t)items_b;
   plan->merge_off = (int64_t)(items_b + waves_b);
   plan->wg_off = (int64_t)(items_b + waves_b + merge_b);
-  plan->zero_off = plan->wg_off + (int64_t)wg_b;
+  plan->append_off = plan->wg_off + (int64_t)wg_b;
+  plan->zero_off = plan->append_off + (int64_t)app_b;
   plan->ml_off = plan->zero_off + (int64_t)zero_b;
   plan->o_off = plan->ml_off + (int64_t)pkv::align_up((size_t)part_cols * 8);
   plan->ws_bytes = (size_t)plan->o_off + (size_t)part_cols * pkv::kHeadDim * 4;
-  plan->host_bytes = items_b + waves_b + merge_b + wg_b + zero_b;
+  plan->host_bytes = items_b + waves_b + merge_b + wg_b + app_b + zero_b;
   if (!h_staging) return PKV_OK;  // size query
   if (h_staging_bytes < plan->host_bytes) return PKV_EWORKSPACE;
   if (ws && ws_bytes < plan->ws_bytes) return PKV_EWORKSPACE;
@@ -311,6 +342,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
   if (!wave_off.empty()) std::memcpy(hs + items_b, wave_off.data(), wave_off.size() * sizeof(int32_t));
   if (!merges.empty()) std::memcpy(hs + items_b + waves_b, merges.data(), merges.size() * sizeof(Merge));
   if (!wg_list.empty()) std::memcpy(hs + plan->wg_off, wg_list.data(), wg_list.size() * sizeof(int32_t));
+  if (!app.empty()) std::memcpy(hs + plan->append_off, app.data(), app.size() * sizeof(int32_t));
   std::memset(hs + plan->zero_off, 0, zero_b);
   if (ws && plan->host_bytes > 0) {
     hipError_t e = hipMemcpyAsync(ws, h_staging, plan->host_bytes, hipMemcpyHostToDevice,

@@ -269,3 +269,53 @@ def test_static_step_rejects_a_plan_larger_than_its_array(lib):
     assert lib.pkv_paged_step_static(*args, None, fake, None) == 1        # no staging: PKV_EINVAL
     args[11] = f32(float("nan"))
     assert lib.pkv_paged_step_static(*args, fake, fake, None) == 1        # bad scale: PKV_EINVAL
+
+
+def _check_append_groups(plan, cu, sl):
+    """The append's row groups tile the packed rows in order, at most 16
+    each, and the rows one sequence appends into one block (a run) always
+    share a group -- checked against each row's position computed here."""
+    cu, sl = np.asarray(cu), np.asarray(sl)
+    T = int(cu[-1])
+    groups = plan.append_groups()
+    assert plan.num_append_groups == len(groups)
+    if T == 0:
+        assert len(groups) == 0
+        return
+    assert groups[0, 0] == 0 and (groups[:, 1] >= 1).all() and (groups[:, 1] <= 16).all()
+    assert (groups[1:, 0] == groups[:-1, 0] + groups[:-1, 1]).all()
+    assert groups[-1, 0] + groups[-1, 1] == T
+    group_of = np.repeat(np.arange(len(groups)), groups[:, 1])
+    seq_of = np.searchsorted(cu, np.arange(T), side="right") - 1
+    pos = sl[seq_of] - (cu[seq_of + 1] - cu[seq_of]) + (np.arange(T) - cu[seq_of])
+    same_run = (seq_of[1:] == seq_of[:-1]) & (pos[1:] // 16 == pos[:-1] // 16)
+    assert (group_of[1:][same_run] == group_of[:-1][same_run]).all()
+    # packing: a group ends early only where the next run would not fit
+    run_start = np.r_[True, ~same_run]
+    run_len = np.diff(np.r_[np.flatnonzero(run_start), T])
+    starts = np.flatnonzero(run_start)
+    for g0, gn in groups[:-1]:
+        nxt = int(np.searchsorted(starts, g0 + gn))
+        assert starts[nxt] == g0 + gn and gn + run_len[nxt] > 16
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_append_groups_keep_block_runs_whole(seed):
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 120))
+    q = np.where(rng.random(S) < 0.6, 1, rng.integers(0, 300, S))
+    cached = rng.integers(0, 5000, S)
+    cu = np.r_[0, np.cumsum(q)].astype(np.int64)
+    sl = (cached + q).astype(np.int64)
+    sl = np.maximum(sl, 1)
+    _check_append_groups(_plan(cu, sl), cu, sl)
+
+
+def test_append_groups_on_the_configs():
+    for name in ("config_worked_step", "config_decode64", "config_mixed_chunked", "config_prefill_fresh"):
+        b = getattr(wl, name)(pool="lazy") if name != "config_worked_step" else wl.config_worked_step()
+        _check_append_groups(_plan(b.cu_seqlens_q, b.seq_lens), b.cu_seqlens_q, b.seq_lens)
+    # block-aligned and unaligned prefill runs, empty sequences, decode rows
+    cu = np.array([0, 16, 16, 17, 50, 51, 67, 100])
+    sl = np.array([16, 3, 9, 48, 17, 32, 1000])
+    _check_append_groups(_plan(cu, sl), cu, sl)
