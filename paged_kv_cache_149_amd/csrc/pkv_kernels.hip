@@ -188,12 +188,14 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 // each.
 // Placement and write policy, both for the launch that follows: runs of 16
 // consecutive row groups go to one XCD (the runs to the XCDs in turn), so
-// the two groups that share a block write it through one L2; and every K/V
-// store is non-temporal, so the step's lines leave the caches during the
-// append.  Plain stores left them to be written back a few at a time while
-// the attention launch streams the pools, and a write under a full read
-// stream costs several times its bytes (on the 200-iteration trace both
-// changes together made the attention launches ~8% faster).
+// the two groups that share a block write it through one L2; and the K
+// stores and paired V stores are non-temporal, so the step's lines leave
+// the caches during the append.  Plain stores left them to be written back
+// a few at a time while the attention launch streams the pools, and a
+// write under a full read stream costs several times its bytes (on the
+// 200-iteration trace both changes together made the attention launches
+// ~8% faster).  With the planner's row groups (pkv_paged_step) every block
+// the step fills is written by one workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kAppendRows = 16;
 constexpr int kAppendRun = 16;  // consecutive row groups per XCD on large steps
@@ -323,8 +325,11 @@ __global__ __launch_bounds__(256) void append_kernel(
     if (pair) {
       __builtin_nontemporal_store(a0 | (a1 << 16), reinterpret_cast<uint32_t *>(vh + (s0 >> 4) * Hkv * TILE + (s0 & 15)));
     } else {
-      if (s0 >= 0) __builtin_nontemporal_store((uint16_t)a0, vh + (s0 >> 4) * Hkv * TILE + (s0 & 15));
-      if (s1 >= 0) __builtin_nontemporal_store((uint16_t)a1, vh + (s1 >> 4) * Hkv * TILE + (s1 & 15));
+      // lone slots (decode rows, run edges) stay plain: non-temporal, each
+      // would leave for HBM at once as a partial line (append 7.5 us slower
+      // per trace step)
+      if (s0 >= 0) vh[(s0 >> 4) * Hkv * TILE + (s0 & 15)] = (uint16_t)a0;
+      if (s1 >= 0) vh[(s1 >> 4) * Hkv * TILE + (s1 & 15)] = (uint16_t)a1;
     }
   }
 }
