@@ -210,8 +210,8 @@ def main():
     def step(i=None):
         if i is not None:
             ev[i][0].record(stream)
-        pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"], t["block_tables"],
-                            t["k_cache"], t["v_cache"], slot_mapping=slots, stream=stream)
+        pkv.pkv_slot_append_planned(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"], t["block_tables"],
+                                    t["k_cache"], t["v_cache"], plan, slot_mapping=slots, stream=stream)
         if i is not None:
             ev[i][1].record(stream)
         pkv.pkv_varlen_attention_main(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["scale"],
@@ -368,8 +368,8 @@ def run_trace(args):
             cu, sl, bt = meta[i]
             ev_it[i][0].record(stream)
             for l in range(L):
-                pkv.pkv_slot_append(ka[l, :T], va[l, :T], cu, sl, bt, kc[l], vc[l], slot_mapping=slots[:T],
-                                    stream=stream)
+                pkv.pkv_slot_append_planned(ka[l, :T], va[l, :T], cu, sl, bt, kc[l], vc[l], plan,
+                                            slot_mapping=slots[:T], stream=stream)
                 ev_at[i][l][0].record(stream)
                 pkv.pkv_varlen_attention_main(qa[l, :T], kc[l], vc[l], bt, scale, plan, out=out[:T], stream=stream)
                 ev_at[i][l][1].record(stream)
@@ -683,8 +683,8 @@ def run_prefix(args):
               for _ in range(args.steps)]
 
         def step(i=None):
-            pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu"], t["sl"], t["bt"], kc, vc,
-                                slot_mapping=slots, stream=stream)
+            pkv.pkv_slot_append_planned(t["k_new"], t["v_new"], t["cu"], t["sl"], t["bt"], kc, vc, plan,
+                                        slot_mapping=slots, stream=stream)
             if i is not None:
                 ev[i][0].record(stream)
             pkv.pkv_varlen_attention_main(t["q"], kc, vc, t["bt"], scale, plan, out=out, stream=stream)
@@ -766,8 +766,8 @@ def run_layer(args):
         mark(0)
         q, k_new, v_new = pkv.pkv_qkv_rope(x, w_qkv, t["cu_seqlens_q"], t["seq_lens"], Hq, Hkv, stream=stream)
         mark(1)
-        pkv.pkv_slot_append(k_new, v_new, t["cu_seqlens_q"], t["seq_lens"], t["block_tables"], t["k_cache"],
-                            t["v_cache"], slot_mapping=slots, stream=stream)
+        pkv.pkv_slot_append_planned(k_new, v_new, t["cu_seqlens_q"], t["seq_lens"], t["block_tables"],
+                                    t["k_cache"], t["v_cache"], plan, slot_mapping=slots, stream=stream)
         mark(2)
         pkv.pkv_varlen_attention_main(q, t["k_cache"], t["v_cache"], t["block_tables"], t["scale"], plan,
                                       out=attn, stream=stream)

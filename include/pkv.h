@@ -258,10 +258,28 @@ int pkv_paged_varlen_attention(const pkv_bf16 *q, const pkv_bf16 *k_cache,
                                pkv_stream_t stream);
 
 /* ---------------------------------------------------------------------------
- * The whole step on one stream: the append of pkv_slot_append (slot_mapping,
- * device int64[T], is written; the same kernel, run on the plan's row groups,
- * so each block the step fills is written by one workgroup), then
- * pkv_paged_varlen_attention.  Attention reads the cache after the append, so
+ * The append of pkv_slot_append on the plan's row groups (plan->append_off
+ * in ws; same slots, slot_mapping written, same pool bytes): the rows one
+ * sequence appends into one block share a workgroup, so every block the step
+ * fills is written in whole lines ("continuous batching" (k4i.top), section
+ * "与 KV cache 的关系": the step's K and V join the cache; "连续批处理与
+ * PagedAttention 原理", section "block table 与地址映射" for the slots).  The
+ * first launch of pkv_paged_step; the plan, the metadata and ws are the
+ * step's.  Errors: PKV_EINVAL (null pointers, a plan whose row groups do not
+ * fit its workspace), PKV_EWORKSPACE (ws_bytes < plan->ws_bytes),
+ * PKV_EUNSUPPORTED (plan head_dim != 128), PKV_EHIP.
+ * ------------------------------------------------------------------------- */
+int pkv_slot_append_planned(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
+                            const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                            const int32_t *block_tables, int32_t bt_stride,
+                            int64_t num_blocks, int64_t *slot_mapping,
+                            pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                            const pkv_plan_t *plan, const void *ws,
+                            size_t ws_bytes, pkv_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The whole step on one stream: pkv_slot_append_planned (slot_mapping,
+ * device int64[T], is written), then pkv_paged_varlen_attention.  Attention reads the cache after the append, so
  * each row sees its own new key.  A scale that is not positive and finite,
  * and a plan whose row groups do not fit its workspace, return PKV_EINVAL
  * before the append is launched.

@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     pkv_paged_varlen_attention,
     pkv_plan,
     pkv_slot_append,
+    pkv_slot_append_planned,
     pkv_slot_mapping,
     swap_bytes,
     pkv_split_kv_reduce,

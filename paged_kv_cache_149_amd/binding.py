@@ -79,6 +79,7 @@ _SIGNATURES = {
     "pkv_split_kv_reduce": (ctypes.c_int, [ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
     "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _F,
                                                   ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
+    "pkv_slot_append_planned": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "pkv_paged_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
                                       ctypes.POINTER(PlanStruct), _P, _SZ, _P, _P]),
     "pkv_paged_step_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P, _F,
@@ -378,6 +379,33 @@ def pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, scale, plan: P
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], nb,
         float(scale), ctypes.byref(plan.st), _ptr(ws), ws.numel(), _ptr(out), _stream(stream, dev)))
     return out
+
+
+def pkv_slot_append_planned(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, k_cache, v_cache, plan: Plan,
+                            slot_mapping=None, stream=None):
+    """pkv_slot_append on the plan's row groups (the step's first launch);
+    returns slot_mapping."""
+    lib = load_library()
+    dev = k_cache.device
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, n, torch.bfloat16, dev)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("seq_lens", seq_lens), ("block_tables", block_tables)):
+        _need(t, n, torch.int32, dev)
+    T, Hkv, D = k_new.shape
+    nb = k_cache.shape[0]
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if T != plan.num_rows or Hkv != plan.num_kv_heads:
+        raise ValueError("k_new does not match the plan")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(T, dtype=torch.int64, device=dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, dev)
+    ws = plan.workspace
+    _check("pkv_slot_append_planned", lib.pkv_slot_append_planned(
+        _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(block_tables), block_tables.shape[1],
+        nb, _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), ctypes.byref(plan.st), _ptr(ws), ws.numel(),
+        _stream(stream, dev)))
+    return slot_mapping
 
 
 def pkv_paged_step(q, k_new, v_new, k_cache, v_cache, cu_seqlens_q, seq_lens, block_tables, scale,

@@ -1996,6 +1996,18 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
                    const pkv_plan_t *plan, void *ws, size_t ws_bytes, pkv_bf16 *out,
                    pkv_stream_t stream) {
   if (!plan || !valid_scale(scale)) return PKV_EINVAL;
+  const int st = pkv_slot_append_planned(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, bt_stride, num_blocks,
+                                         slot_mapping, k_cache, v_cache, plan, ws, ws_bytes, stream);
+  if (st != PKV_OK) return st;
+  return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
+                                    scale, plan, ws, ws_bytes, out, stream);
+}
+
+int pkv_slot_append_planned(const pkv_bf16 *k_new, const pkv_bf16 *v_new, const int32_t *cu_seqlens_q,
+                            const int32_t *seq_lens, const int32_t *block_tables, int32_t bt_stride,
+                            int64_t num_blocks, int64_t *slot_mapping, pkv_bf16 *k_cache, pkv_bf16 *v_cache,
+                            const pkv_plan_t *plan, const void *ws, size_t ws_bytes, pkv_stream_t stream) {
+  if (!plan) return PKV_EINVAL;
   // pkv_slot_append's checks, then its kernel on the plan's row groups
   const int32_t S = plan->num_seqs, T = plan->num_rows, Hkv = plan->num_kv_heads;
   if (S < 0 || T < 0 || bt_stride < 0 || num_blocks < 0 || Hkv <= 0) return PKV_EINVAL;
@@ -2011,11 +2023,9 @@ int pkv_paged_step(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_n
     launch_append(k_new, v_new, nullptr, cu_seqlens_q, seq_lens, block_tables, bt_stride, S, T, Hkv, num_blocks,
                   slot_mapping, k_cache, v_cache, as_stream(stream),
                   reinterpret_cast<const int2 *>(static_cast<const char *>(ws) + plan->append_off), ng);
-    const int st = launch_status();
-    if (st != PKV_OK) return st;
+    return launch_status();
   }
-  return pkv_paged_varlen_attention(q, k_cache, v_cache, block_tables, bt_stride, num_blocks,
-                                    scale, plan, ws, ws_bytes, out, stream);
+  return PKV_OK;
 }
 
 int pkv_paged_step_static(const pkv_bf16 *q, const pkv_bf16 *k_new, const pkv_bf16 *v_new,

@@ -472,3 +472,39 @@ def test_trace_steps_around_a_preemption(dev):
         b = wl.batch_from_metadata(f"preempt-step{st.index}", st.cu_seqlens_q, st.seq_lens, st.block_tables,
                                    16384, seed=149500 + st.index)
         run_whole(b, dev, f"preemption trace step {st.index} (whole)")
+
+
+@pytest.mark.parametrize("name", ["trace-step150", "edge-runs"])
+def test_planned_append_equals_plain_append(dev, trace_steps, name):
+    """pkv_slot_append_planned (the step's append, on the planner's row
+    groups) writes the same slots and leaves both pools bit-identical to
+    pkv_slot_append (16-row groups); both checked against the oracle."""
+    if name == "trace-step150":
+        st = trace_steps[150]
+        b = wl.batch_from_metadata("trace-step150-append", st.cu_seqlens_q, st.seq_lens, st.block_tables,
+                                   65536, seed=149777)
+    else:
+        # (cached, new rows): runs that start and end inside blocks, a
+        # block-aligned run, empty sequences and lone decode rows between them
+        b = wl.make_batch("edge-runs-append", [(0, 16), (3, 0), (8, 1), (15, 33), (16, 1), (16, 16), (967, 33),
+                                               (6, 1), (0, 0), (5, 39), (1, 1)], seed=149778)
+    note(f"planned append {name}: {b.num_rows} rows, {b.num_seqs} sequences")
+    plan = pkv.pkv_plan(b.cu_seqlens_q, b.seq_lens, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                        block_tables=b.block_tables, num_blocks=b.num_blocks, device=dev)
+    assert plan.num_append_groups > 0
+    results = []
+    for planned in (False, True):
+        t = to_device(b, dev)
+        if planned:
+            slots = pkv.pkv_slot_append_planned(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"],
+                                                t["block_tables"], t["k_cache"], t["v_cache"], plan)
+        else:
+            slots = pkv.pkv_slot_append(t["k_new"], t["v_new"], t["cu_seqlens_q"], t["seq_lens"],
+                                        t["block_tables"], t["k_cache"], t["v_cache"])
+        torch.cuda.synchronize()
+        s = slots.cpu().numpy()
+        check_append(b, s, t)
+        results.append((s, t["k_cache"].view(torch.int16).clone(), t["v_cache"].view(torch.int16).clone()))
+        del t
+    assert np.array_equal(results[0][0], results[1][0])
+    assert torch.equal(results[0][1], results[1][1]) and torch.equal(results[0][2], results[1][2])
