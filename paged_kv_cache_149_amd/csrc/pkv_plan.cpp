@@ -8,10 +8,11 @@
 //    wide tile (256 columns: 256/G positions x G heads) is computed by a
 //    whole workgroup of eight wavefronts sharing K/V through LDS.  The
 //    launch has a fixed set of persistent workgroups; the wide tiles are
-//    dealt to them longest first, each to the least loaded workgroup (with
-//    the estimated time of its narrow share as its starting load), tiles of
-//    kv head h to the workgroups on XCD h % 8, so a head's keys and values
-//    are fetched from HBM into one L2.
+//    dealt to them in pairs of equal cost (tiles j and n - 1 - j of one
+//    sequence and kv head), longest first, each to the least loaded
+//    workgroup (with the estimated time of its narrow share as its starting
+//    load), tiles of kv head h to the workgroups on XCD h % 8, so a head's
+//    keys and values are fetched from HBM into one L2.
 //  * Decode rows and the short tails of prefill rows: narrow (<= 16 column)
 //    units (tile, kv head), each a stream of 32-key chunks.  All chunks of all
 //    units are dealt out in equal contiguous shares to a fixed number of
@@ -227,17 +228,55 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     }
     // tiles of kv head h go to XCD h % 8 when every XCD gets whole heads
     const bool affine = Hkv % kXcds == 0;
-    std::vector<int> order(n_wide);
-    for (int i = 0; i < n_wide; ++i) order[i] = i;
-    auto cost = [&](int i) { return kWideChunkUs * ((items[i].k1 + 31) / 32) + kWideTileUs; };
-    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return cost(x) > cost(y); });
+    // Dealing units: the n tiles of one (sequence, kv head) cost a + b j
+    // (causal: each takes 256/G more keys than the one before), so tiles j
+    // and n - 1 - j always sum to the same cost; they go to a workgroup as
+    // a pair, the longer first.  Equal-cost units keep their order
+    // (sequence, kv head, j), so the workgroups of an XCD take a prompt's
+    // pairs side by side and stream its keys and values nearly in step
+    // through one L2, one or two prompts at a time (dealt one tile at a
+    // time, longest first, the XCD's L2 held every prompt of its kv head at
+    // once and refetched their keys: 1.29 x the algorithmic bytes on four
+    // fresh 2048-token prompts).
+    // Only with at least two tiles per workgroup: with fewer, every tile of
+    // a head runs at once on its XCD (sharing its keys through L2 anyway)
+    // and pairs would leave workgroups idle (a 2048-token chunk after a
+    // 30,720-token prefix: 32 tiles per kv head on 32 CUs, 894 -> 1518 us
+    // as pairs).  Costs are compared as whole chunk and tile counts, so
+    // equal pairs tie exactly and keep their order.
+    const bool pairs = (int64_t)n_wide >= 2 * (int64_t)n_wg;
+    struct Unit { int a, b, chunks, tiles; double c; };  // items (b < 0: none), cost
+    auto chunks = [&](int i) { return (items[i].k1 + 31) / 32; };
+    std::vector<Unit> units;
+    for (int t0 = 0; t0 < (int)wide_tiles.size();) {
+      int t1 = t0;
+      while (t1 < (int)wide_tiles.size() && wide_tiles[t1].seq == wide_tiles[t0].seq) ++t1;
+      const int n = t1 - t0;
+      for (int h = 0; h < Hkv; ++h) {
+        for (int k = 0; k < (n + 1) / 2; ++k) {
+          const int lo = (t0 + k) * Hkv + h, hi = (t1 - 1 - k) * Hkv + h;
+          if (lo == hi || !pairs) {
+            units.push_back(Unit{hi, -1, chunks(hi), 1, kWideChunkUs * chunks(hi) + kWideTileUs});
+            if (lo != hi) units.push_back(Unit{lo, -1, chunks(lo), 1, kWideChunkUs * chunks(lo) + kWideTileUs});
+          } else {
+            const int c = chunks(hi) + chunks(lo);
+            units.push_back(Unit{hi, lo, c, 2, kWideChunkUs * c + 2 * kWideTileUs});
+          }
+        }
+      }
+      t0 = t1;
+    }
+    std::stable_sort(units.begin(), units.end(), [](const Unit &x, const Unit &y) {
+      return x.chunks != y.chunks ? x.chunks > y.chunks : x.tiles > y.tiles;
+    });
     std::vector<std::vector<int>> lists(n_wg);
-    for (int i : order) {
+    for (const Unit &u : units) {
       int best = -1;
-      for (int j = affine ? items[i].kvh % kXcds : 0; j < n_wg; j += affine ? kXcds : 1)
+      for (int j = affine ? items[u.a].kvh % kXcds : 0; j < n_wg; j += affine ? kXcds : 1)
         if (best < 0 || load[j] < load[best]) best = j;
-      load[best] += cost(i);
-      lists[best].push_back(i);
+      load[best] += u.c;
+      lists[best].push_back(u.a);
+      if (u.b >= 0) lists[best].push_back(u.b);
     }
     std::vector<Item> wide(items.begin(), items.begin() + n_wide);
     wg_list.push_back(0);
