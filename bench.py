@@ -316,7 +316,7 @@ def run_trace(args):
     log(f"trace: {n_it} iterations, {L} layers, {NB}-block pool per layer, "
         f"{sch.preemptions} preemptions, {len(sch.finished)} requests finished (scheduler {sched_s:.2f} s)")
     kc = [torch.empty(NB, Hkv, 16, D, dtype=torch.bfloat16, device=dev) for _ in range(L)]
-    vc = [torch.empty(NB, Hkv, D, 16, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    vc = [torch.empty(pkv.v_cache_shape(NB, Hkv, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     Tmax = max(st.num_rows for st in steps)
     qa = torch.empty(L, Tmax, Hq, D, dtype=torch.bfloat16, device=dev)
     ka = torch.empty(L, Tmax, Hkv, D, dtype=torch.bfloat16, device=dev)
@@ -554,7 +554,7 @@ def run_blocks(args):
     pkv.load_library()
     Hkv, D, nb = 8, 128, 16384
     kc = torch.empty(nb, Hkv, 16, D, dtype=torch.bfloat16, device=dev).normal_()
-    vc = torch.empty(nb, Hkv, D, 16, dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty(pkv.v_cache_shape(nb, Hkv, D), dtype=torch.bfloat16, device=dev).normal_()
     perm = np.random.default_rng(149100).permutation(nb).astype(np.int32)
     blk = 2 * Hkv * 16 * D * 2
     stream = torch.cuda.current_stream(dev)
@@ -632,7 +632,7 @@ def run_prefix(args):
     pool = pkv.BlockPool(nb)
     cap = 140
     kc = torch.empty(nb, Hkv, 16, D, dtype=torch.bfloat16, device=dev).normal_()
-    vc = torch.empty(nb, Hkv, D, 16, dtype=torch.bfloat16, device=dev).normal_()
+    vc = torch.empty(pkv.v_cache_shape(nb, Hkv, D), dtype=torch.bfloat16, device=dev).normal_()
     stream = torch.cuda.current_stream(dev)
     scale = 1.0 / np.sqrt(D)
 

@@ -36,11 +36,14 @@
  * block's 16 tokens are contiguous; they leave the tensor layout open):
  *   k_cache : bf16[num_blocks][Hkv][4][16][32]  4 KiB tiles: four groups of
  *             32 dimensions, each group token-major
- *   v_cache : bf16[num_blocks][Hkv][128][16]    dimension-major 4 KiB tiles
+ *   v_cache : bf16[num_blocks][Hkv][2][128][8]  4 KiB tiles: two halves of
+ *             8 tokens, each half dimension-major
  * Slot x is block x / 16, offset x % 16.  Key element (o, d) of a tile sits
- * at (d / 32) * 512 + o * 32 + d % 32; value element (o, d) at d * 16 + o.
- * (Both orders let a 16-byte-per-lane load over 16 tokens read whole cache
- * lines in the operand order of the bf16 MFMAs.)
+ * at (d / 32) * 512 + o * 32 + d % 32; value element (o, d) at
+ * (o / 8) * 1024 + d * 8 + o % 8.  (Both orders let a 16-byte-per-lane load
+ * over 16 tokens read whole cache lines in the operand order of the bf16
+ * MFMAs; the halves make a lone appended token touch 64 of the value tile's
+ * 32-byte sectors, not 128.)
  *
  * Packed tensors:
  *   q        : bf16[T][Hq][128]      k_new, v_new : bf16[T][Hkv][128]

@@ -33,8 +33,9 @@ the design notes):
   tensor layout to a section that is not present): K tiles hold the
   dimensions in groups of W = min(32, D), each group token-major: element
   (o, d) at ``(d // W) * 16 * W + o * W + d % W`` (D = 128: four groups of
-  32 dimensions); V tiles are dimension-major, element (o, d) at
-  ``d * 16 + o``.  Slot ``x`` is block ``x // 16``, offset ``x % 16``.
+  32 dimensions); V tiles hold the 16 tokens in two halves of 8, each half
+  dimension-major: element (o, d) at ``(o // 8) * 8 * D + d * 8 + o % 8``.
+  Slot ``x`` is block ``x // 16``, offset ``x % 16``.
 * Masked scores are -inf (the M_ij formula of [K4I]); every row sees at
   least its own key, so no row is fully masked.
 
@@ -106,12 +107,16 @@ def read_k_token(k_pool: np.ndarray, slot: int, head: int, D: int) -> np.ndarray
     return tile[:, o, :].reshape(D)
 
 
+V_HALF = 8  # tokens per half of a V tile
+
+
 def read_v_token(v_pool: np.ndarray, slot: int, head: int, D: int) -> np.ndarray:
-    """The D value elements at ``slot`` for kv head ``head`` (bf16 bits);
-    the V tile is dimension-major so they sit 16 elements apart."""
+    """The D value elements at ``slot`` for kv head ``head`` (bf16 bits):
+    in the half holding token o, they sit 8 elements apart."""
     b, o = divmod(int(slot), BLOCK)
-    tile = v_pool[b, head]
-    return tile[o::BLOCK][:D]
+    tile = np.asarray(v_pool[b, head])
+    start = (o // V_HALF) * V_HALF * D + o % V_HALF
+    return tile[start:start + V_HALF * D:V_HALF]
 
 
 def gather_kv(k_pool, v_pool, block_table_row, n_tokens: int, H_kv: int, D: int):
@@ -126,9 +131,9 @@ def gather_kv(k_pool, v_pool, block_table_row, n_tokens: int, H_kv: int, D: int)
     blocks = np.asarray(block_table_row[:nblk], dtype=np.int64)
     W = k_group(D)
     kt = k_pool[blocks].reshape(nblk, H_kv, D // W, BLOCK, W)   # (blk, h, group, o, d % W)
-    vt = v_pool[blocks].reshape(nblk, H_kv, D, BLOCK)            # (blk, h, d, o)
+    vt = v_pool[blocks].reshape(nblk, H_kv, BLOCK // V_HALF, D, V_HALF)  # (blk, h, half, d, o % 8)
     K = kt.transpose(0, 3, 1, 2, 4).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
-    V = vt.transpose(0, 3, 1, 2).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
+    V = vt.transpose(0, 2, 4, 1, 3).reshape(nblk * BLOCK, H_kv, D)[:n_tokens]
     return bf16_bits_to_f64(K), bf16_bits_to_f64(V)
 
 
@@ -160,7 +165,8 @@ def pools_after_append(k_pool, v_pool, slots, k_new, v_new):
         W = k_group(D)
         for h in range(H_kv):
             k_out[b, h].reshape(D // W, BLOCK, W)[:, o, :] = np.asarray(k_new[t, h]).reshape(D // W, W)
-            v_out[b, h, o::BLOCK][:D] = v_new[t, h]
+            start = (o // V_HALF) * V_HALF * D + o % V_HALF
+            v_out[b, h, start:start + V_HALF * D:V_HALF] = v_new[t, h]
     return k_out, v_out
 
 

@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     pkv_slot_append_planned,
     pkv_slot_mapping,
     swap_bytes,
+    v_cache_shape,
     pkv_split_kv_reduce,
     pkv_swap_in,
     pkv_swap_out,

@@ -23,6 +23,12 @@ from ._build import LIB_PATH, INCLUDE
 
 BLOCK_SIZE = 16
 HEAD_DIM = 128
+V_HALF = 8  # a V tile holds its block's tokens in two halves of 8, each [D][8]
+
+
+def v_cache_shape(num_blocks: int, num_kv_heads: int, head_dim: int = HEAD_DIM) -> tuple:
+    """Shape of the V pool tensor: [NB][Hkv][2][D][8] (see include/pkv.h)."""
+    return (num_blocks, num_kv_heads, BLOCK_SIZE // V_HALF, head_dim, V_HALF)
 ITEM_INTS = 8
 MERGE_INTS = 4
 
@@ -199,8 +205,8 @@ def pkv_paged_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=Non
     _need(slot_mapping, "slot_mapping", torch.int64, dev)
     T, Hkv, D = k_new.shape
     nb = k_cache.shape[0]
-    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
-        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != v_cache_shape(nb, Hkv, D):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,2,D,8] (V)")
     if v_new.shape != k_new.shape or slot_mapping.shape[0] != T:
         raise ValueError("row counts differ")
     _check("pkv_paged_kv_append", lib.pkv_paged_kv_append(
@@ -219,8 +225,8 @@ def pkv_slot_append(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, k_cache,
         _need(t, n, torch.int32, dev)
     T, Hkv, D = k_new.shape
     nb = k_cache.shape[0]
-    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
-        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != v_cache_shape(nb, Hkv, D):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,2,D,8] (V)")
     if slot_mapping is None:
         slot_mapping = torch.empty(T, dtype=torch.int64, device=dev)
     _need(slot_mapping, "slot_mapping", torch.int64, dev)
@@ -340,8 +346,8 @@ def _attn_args(q, k_cache, v_cache, block_tables, plan: Plan, out):
     nb, Hkv = k_cache.shape[0], k_cache.shape[1]
     if Hkv != plan.st.num_kv_heads:
         raise ValueError("kv heads do not match the plan")
-    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
-        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != v_cache_shape(nb, Hkv, D):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,2,D,8] (V)")
     if block_tables.shape[0] != plan.st.num_seqs:
         raise ValueError("block_tables rows do not match the plan")
     if out is None:
@@ -393,8 +399,8 @@ def pkv_slot_append_planned(k_new, v_new, cu_seqlens_q, seq_lens, block_tables, 
         _need(t, n, torch.int32, dev)
     T, Hkv, D = k_new.shape
     nb = k_cache.shape[0]
-    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
-        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != v_cache_shape(nb, Hkv, D):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,2,D,8] (V)")
     if T != plan.num_rows or Hkv != plan.num_kv_heads:
         raise ValueError("k_new does not match the plan")
     if slot_mapping is None:
@@ -638,8 +644,8 @@ def pkv_block_hash(parent: int, tokens16, extra_key: int = 0) -> int:
 
 def _pool_shapes(k_cache, v_cache):
     nb, Hkv, _, D = k_cache.shape
-    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != (nb, Hkv, D, BLOCK_SIZE):
-        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,D,16] (V)")
+    if k_cache.shape != (nb, Hkv, BLOCK_SIZE, D) or v_cache.shape != v_cache_shape(nb, Hkv, D):
+        raise ValueError("cache shapes must be [NB,Hkv,16,D] (K) and [NB,Hkv,2,D,8] (V)")
     return nb, Hkv, D
 
 

@@ -22,9 +22,9 @@
 //   C[m][n]: lane holds C[4g .. 4g+3][r]
 // Keys are assigned to the rows of the two S^T tiles so that lane group g's
 // eight C values are keys 8g .. 8g+7 of the step, exactly the slots it needs
-// as the B operand (P^T) of the P.V product.  The V tile of a block is
-// stored dimension-major (16 tokens contiguous per dimension), so the V^T A
-// operand is one 16-byte load per lane; K tiles hold 32-dimension groups,
+// as the B operand (P^T) of the P.V product.  The V tile of a block holds
+// its tokens in two halves of 8, each dimension-major (8 tokens contiguous
+// per dimension), so the V^T A operand is one 16-byte load per lane; K tiles hold 32-dimension groups,
 // each token-major, so the K A operand is one 16-byte load per lane per 32
 // dimensions and every load reads whole cache lines.  Narrow items load
 // their operands straight from HBM in MFMA layout; wide tiles stage each
@@ -58,6 +58,13 @@ constexpr int TILE = pkv::kBlock * pkv::kHeadDim;  // elements of a (block, head
 constexpr int kKGroup = 32;
 constexpr int kKGroupElems = pkv::kBlock * kKGroup;
 constexpr int kXcdCount = 8;  // XCDs of an MI355X; consecutive workgroups go to them in turn
+// V tiles hold the block's tokens in two halves of 8, each half
+// dimension-major: element (o, d) at (o / 8) * 8 * 128 + d * 8 + o % 8, so a
+// lane's V^T operand (8 consecutive keys of one dimension) is one 16-byte
+// load, and a row appended alone touches 64 of the tile's 32-byte sectors
+// (two dimensions per sector) rather than 128.
+constexpr int kVHalf = 8;                       // tokens per half
+constexpr int kVHalfElems = kVHalf * pkv::kHeadDim;  // elements per half (1024)
 
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -180,12 +187,11 @@ __device__ inline int wave_seq_of_row(const int32_t *__restrict__ cu, int S, int
 // a prefix of the window); a row more than 63 sequence boundaries past the
 // first -- only possible across empty sequences -- takes the plain binary
 // search.  K rows: lanes run over dimensions, each row's 256 bytes are four
-// 64-byte stores, one per 32-dimension group of the tile.  V tiles are
-// dimension-major (a block's 16 tokens contiguous per dimension): lanes run
-// over rows, so each store instruction writes, per dimension, the
-// consecutive slots of up to 16 consecutive rows -- whole sectors inside any
-// prefill run, whatever its alignment; decode rows touch one slot of a block
-// each.
+// 64-byte stores, one per 32-dimension group of the tile.  V tiles hold
+// two halves of 8 tokens, each dimension-major: lanes run over rows, so each
+// store instruction writes, per dimension, the consecutive slots of up to 8
+// consecutive rows in each half -- whole 16-byte pieces inside any prefill
+// run; decode rows touch one slot of a block each (64 sectors of the tile).
 // Placement and write policy, both for the launch that follows: runs of 16
 // consecutive row groups go to one XCD (the runs to the XCDs in turn), so
 // the two groups that share a block write it through one L2; and the K
@@ -222,7 +228,11 @@ __global__ __launch_bounds__(256) void append_kernel(
     if (grp >= ngroups) return;  // padding of the grid
     const int2 gd = groups[grp];
     t0 = gd.x;
-    n = gd.y;
+    // a list that does not fit the batch (not the plan's) touches no row
+    // outside it
+    if (t0 < 0 || t0 >= T) return;
+    n = min(min(gd.y, kAppendRows), T - t0);
+    if (n <= 0) return;
   } else {
     t0 = grp * kAppendRows;
     if (t0 >= T) return;  // padding of the grid
@@ -307,10 +317,11 @@ __global__ __launch_bounds__(256) void append_kernel(
         if (j < nh) __builtin_nontemporal_store(xk[j], reinterpret_cast<u32x4 *>(kp + j * TILE));
     }
   }
-  // V, dimension-major: lanes over (row pair, dimension), pairs fastest, so a
-  // wavefront's stores cover 8 dimensions x 16 tokens -- 32 contiguous bytes
-  // per dimension when the rows fill a block in order; a pair of
-  // consecutive, 4-byte-aligned slots is one 4-byte store
+  // V, halves of 8 tokens, dimension-major: lanes over (row pair, dimension),
+  // pairs fastest, so a wavefront's stores cover 8 dimensions x 16 tokens --
+  // 128 contiguous bytes per half when the rows fill a block in order; a
+  // pair of consecutive, 4-byte-aligned slots (never split between halves)
+  // is one 4-byte store
   const int p = tid & 7;  // this thread's row pair, the same in every round below
   const int r0 = 2 * p, r1 = r0 + 1;
   const int64_t s0 = r0 < n ? srow[r0] : -1, s1 = r1 < n ? srow[r1] : -1;
@@ -321,15 +332,17 @@ __global__ __launch_bounds__(256) void append_kernel(
     if (j >= nh) continue;
     const uint32_t w0 = vrow[j][r0][d >> 1], w1 = vrow[j][r1][d >> 1];
     const uint32_t a0 = d & 1 ? w0 >> 16 : w0 & 0xFFFF, a1 = d & 1 ? w1 >> 16 : w1 & 0xFFFF;
-    uint16_t *vh = vc + (int64_t)(h0 + j) * TILE + (int64_t)d * pkv::kBlock;
+    uint16_t *vh = vc + (int64_t)(h0 + j) * TILE + (int64_t)d * kVHalf;
+    // slot sl's element of this dimension
+    auto at = [&](int64_t sl) { return vh + (sl >> 4) * Hkv * TILE + ((sl & 15) >> 3) * kVHalfElems + (sl & 7); };
     if (pair) {
-      __builtin_nontemporal_store(a0 | (a1 << 16), reinterpret_cast<uint32_t *>(vh + (s0 >> 4) * Hkv * TILE + (s0 & 15)));
+      __builtin_nontemporal_store(a0 | (a1 << 16), reinterpret_cast<uint32_t *>(at(s0)));
     } else {
       // lone slots (decode rows, run edges) stay plain: non-temporal, each
       // would leave for HBM at once as a partial line (append 7.5 us slower
       // per trace step)
-      if (s0 >= 0) vh[(s0 >> 4) * Hkv * TILE + (s0 & 15)] = (uint16_t)a0;
-      if (s1 >= 0) vh[(s1 >> 4) * Hkv * TILE + (s1 & 15)] = (uint16_t)a1;
+      if (s0 >= 0) *at(s0) = (uint16_t)a0;
+      if (s1 >= 0) *at(s1) = (uint16_t)a1;
     }
   }
 }
@@ -428,7 +441,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
   const int k_sel = ka >> 1;                         // which block of the pair
   const int k_row_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g;  // + 4*mt*kKGroup + c*kKGroupElems
   const int v_sel = g >> 1;
-  const int v_off = r * pkv::kBlock + 8 * (g & 1);         // + 16*dt*16
+  const int v_off = r * kVHalf + kVHalfElems * (g & 1);  // + 16*dt*8
 
   // Chunk cc covers keys k0 + 32cc .. +31 in logical blocks kb0 + 2cc and
   // kb0 + 2cc + 1.  When the second block is not needed it aliases the
@@ -451,7 +464,7 @@ __device__ __forceinline__ void run_item(const AttnArgs &a, const Item &it) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * kKGroup + c * kKGroupElems);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * pkv::kBlock);
+    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * kVHalf);
     ch.bad0 = !ok0;
     ch.bad1 = need1 && !ok1;
   };
@@ -679,7 +692,7 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
   const int k_sel = ka >> 1;
   const int k_row_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g;
   const int v_sel = g >> 1;
-  const int v_off = r * pkv::kBlock + 8 * (g & 1);
+  const int v_off = r * kVHalf + kVHalfElems * (g & 1);
   const int64_t blk_stride = (int64_t)a.Hkv * TILE;
 
   // ---- load cursor (wave-uniform): item li (fields itL, nchL chunks), its
@@ -744,7 +757,7 @@ __device__ __forceinline__ void narrow_stream(const AttnArgs &a, int i0, int i1,
 #pragma unroll
       for (int c = 0; c < 4; ++c) ch.k[mt * 4 + c] = load16_stream(kp + 4 * mt * kKGroup + c * kKGroupElems);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * pkv::kBlock);
+    for (int dt = 0; dt < 8; ++dt) ch.v[dt] = load16_stream(vp + dt * 16 * kVHalf);
     ch.bad0 = !ok0;
     ch.bad1 = need1 && !ok1;
   };
@@ -1114,7 +1127,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
       lane_off = (8 * (ka & 1) + kbb) * kKGroup + 8 * g + 4 * (R0 >> 2) * kKGroup + (R0 & 3) * kKGroupElems;
     } else {      // region R: 16-dim tile R-8
       sel = g >> 1;
-      lane_off = r * pkv::kBlock + 8 * (g & 1) + (R0 - 8) * 16 * pkv::kBlock;
+      lane_off = r * kVHalf + kVHalfElems * (g & 1) + (R0 - 8) * 16 * kVHalf;
     }
   }
   auto slot = [&](int c) -> u32x4 * { return lds_chunks + (c & (kNbuf - 1)) * kChunkVec; };
@@ -1154,7 +1167,7 @@ __device__ __forceinline__ void run_wide_list(const AttnArgs &a, int i0, int i1)
     const uint16_t *src = (sel ? tile(b1) : tile(b0)) + lane_off;
     u32x4 *dst = slot(n_issued) + w * RPW * 64;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src + (kside ? kKGroupElems : 16 * pkv::kBlock), (lds_void_t *)(dst + 64), 16, 0,
+    __builtin_amdgcn_global_load_lds(src + (kside ? kKGroupElems : 16 * kVHalf), (lds_void_t *)(dst + 64), 16, 0,
                                      0);
     ++n_issued;
     const bool live = ci < i1;

@@ -1,7 +1,7 @@
 """Put a generated batch on a GPU in the shapes the library takes.
 
-A pool tile of 2048 elements is viewed as [16][128] for keys and [128][16]
-for values (no data moves); lazily defined pools are generated directly on
+A pool tile of 2048 elements is viewed as [16][128] for keys and [2][128][8]
+for values (two halves of 8 tokens; no data moves); lazily defined pools are generated directly on
 the device from the counter definition.
 """
 
@@ -29,7 +29,7 @@ def to_device(batch, device) -> dict:
     nb, hkv, tile = batch.k_pool.shape
     assert tile == 16 * D
     k = pool_to_device(batch.k_pool, device).view(nb, hkv, 16, D)
-    v = pool_to_device(batch.v_pool, device).view(nb, hkv, D, 16)
+    v = pool_to_device(batch.v_pool, device).view(nb, hkv, 2, D, 8)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
     return dict(
         q=bf16_from_bits(batch.q, device),

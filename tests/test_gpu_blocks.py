@@ -45,7 +45,7 @@ def _pools(nb, hkv=8, seed=3, normal=False):
 def _to_dev(k, v, dev):
     nb, hkv = k.shape[:2]
     kc = pkv.bf16_tensor(k, dev).view(nb, hkv, 16, 128)
-    vc = pkv.bf16_tensor(v, dev).view(nb, hkv, 128, 16)
+    vc = pkv.bf16_tensor(v, dev).view(nb, hkv, 2, 128, 8)
     return kc, vc
 
 

@@ -84,7 +84,8 @@ def check_append(batch, slots, t, blocks=None):
         b, o = divmod(int(x), 16)
         for h in range(batch.num_kv_heads):
             k_exp[pos[b], h].reshape(D // W, 16, W)[:, o, :] = batch.k_new[row, h].reshape(D // W, W)
-            v_exp[pos[b], h, o::16][:D] = batch.v_new[row, h]
+            start = (o // 8) * 8 * D + o % 8  # V tile: halves of 8 tokens, each [D][8]
+            v_exp[pos[b], h, start:start + 8 * D:8] = batch.v_new[row, h]
     assert np.array_equal(k_dev.reshape(k_exp.shape), k_exp)
     assert np.array_equal(v_dev.reshape(v_exp.shape), v_exp)
 
@@ -346,7 +347,7 @@ def test_nan_in_unused_slots_does_not_leak(dev):
         W = oracle.k_group(D)
         for o in range(n % 16 or 16, 16):
             b.k_pool[last].reshape(b.num_kv_heads, D // W, 16, W)[:, :, o, :] = 0x7FC0
-            b.v_pool[last, :, o::16] = 0x7FC0
+            b.v_pool[last, :, (o // 8) * 8 * D + o % 8::8][:, :D] = 0x7FC0
     out, _, _, _ = run_step(b, dev)
     check_attention(out, oracle.packed_attention(b), "nan tails")
 

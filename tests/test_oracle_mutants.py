@@ -91,6 +91,17 @@ def test_pins_catch_wrong_v_tile_reading(monkeypatch):
         pins.test_gather_blockwise_equals_token_by_token()
 
 
+def test_pins_catch_whole_tile_dimension_major_v_reading(monkeypatch):
+    # the V tile as one [D][16] dimension-major block instead of two halves
+    def whole_tile_v(v_pool, slot, head, D):
+        b, o = divmod(int(slot), 16)
+        return np.asarray(v_pool[b, head])[o::16][:D]
+
+    monkeypatch.setattr(pa, "read_v_token", whole_tile_v)
+    with pytest.raises(AssertionError):
+        pins.test_gather_blockwise_equals_token_by_token()
+
+
 def test_pins_catch_token_major_k_reading(monkeypatch):
     def token_major_k(k_pool, slot, head, D):
         b, o = divmod(int(slot), 16)

@@ -157,8 +157,9 @@ def test_append_round_trip_and_untouched_tiles():
             expect.add((int(x) // 16, h, int(x) % 16))
     assert touched <= expect  # identical values may coincide; nothing else moved
     changed_v = np.argwhere(v2 != b.v_pool)
-    for blk, h, e in changed_v:
-        assert (int(blk), int(h), int(e) % 16) in expect
+    for blk, h, e in changed_v:  # V tile: halves of 8 tokens, each [D][8]
+        o = (int(e) // (8 * 16)) * 8 + int(e) % 8
+        assert (int(blk), int(h), o) in expect
     # the skipped row's slot kept its old contents
     x = int(slots[1])
     assert np.array_equal(k2[x // 16, :, (x % 16) * 16:(x % 16 + 1) * 16],
