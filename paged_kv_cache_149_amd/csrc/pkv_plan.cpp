@@ -244,7 +244,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
     // 30,720-token prefix: 32 tiles per kv head on 32 CUs, 894 -> 1518 us
     // as pairs).  Costs are compared as whole chunk and tile counts, so
     // equal pairs tie exactly and keep their order.
-    const bool pairs = (int64_t)n_wide >= 2 * (int64_t)n_wg;
+    const bool deal_pairs = (int64_t)n_wide >= 2 * (int64_t)n_wg;
     struct Unit { int a, b, chunks, tiles; double c; };  // items (b < 0: none), cost
     auto chunks = [&](int i) { return (items[i].k1 + 31) / 32; };
     std::vector<Unit> units;
@@ -255,7 +255,7 @@ extern "C" int pkv_plan(const int32_t *h_cu, const int32_t *h_seq_lens,
       for (int h = 0; h < Hkv; ++h) {
         for (int k = 0; k < (n + 1) / 2; ++k) {
           const int lo = (t0 + k) * Hkv + h, hi = (t1 - 1 - k) * Hkv + h;
-          if (lo == hi || !pairs) {
+          if (lo == hi || !deal_pairs) {
             units.push_back(Unit{hi, -1, chunks(hi), 1, kWideChunkUs * chunks(hi) + kWideTileUs});
             if (lo != hi) units.push_back(Unit{lo, -1, chunks(lo), 1, kWideChunkUs * chunks(lo) + kWideTileUs});
           } else {
