@@ -140,7 +140,9 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * (256 columns: up to 256/G positions) is computed by one whole workgroup.
  * The launch has a fixed set of persistent workgroups (rows of eight, one
  * per CU); each walks a list of wide tiles that the plan deals out longest
- * first to the least loaded workgroup, tiles of kv head h to the workgroups
+ * first to the least loaded workgroup -- with at least two tiles per
+ * workgroup as pairs of equal cost (tiles j and n - 1 - j of one sequence
+ * and kv head), the longer first -- tiles of kv head h to the workgroups
  * of XCD h % 8 when Hkv is a multiple of 8.  Everything else -- decode rows and
  * short tiles ("11.2 连续批处理与 PagedAttention", section 11.2.2: attention
  * runs per request inside one launch) -- is a (tile, kv head) unit whose
@@ -148,6 +150,9 @@ int pkv_slot_append(const pkv_bf16 *k_new, const pkv_bf16 *v_new,
  * equal contiguous shares to a fixed number of wavefronts, splitting a unit
  * wherever a share ends, so every wavefront streams the same number of
  * bytes however ragged the contexts are.  Split units are merged afterwards.
+ * The plan also cuts the packed rows into the append's row groups (at most
+ * 16 consecutive rows; the rows one sequence appends into one block never
+ * split), which pkv_slot_append_planned and pkv_paged_step use.
  *
  * The plan is written to h_staging (host memory; pinned memory lets the copy
  * run asynchronously) and, when ws is not NULL, copied to ws with
