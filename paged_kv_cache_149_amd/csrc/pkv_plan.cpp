@@ -43,7 +43,11 @@ constexpr int kDefaultWorkgroups = 256;    // one per CU on an MI355X
 constexpr int kXcds = 8;                   // consecutive workgroups go to the XCDs in turn
 
 // Cost model of the launch with wide tiles, in CU-microseconds (measured on
-// MI355X): a wide tile costs ~0.9 us per 32-key chunk plus ~2 us to start.
+// MI355X): a wide tile costs ~0.8 us per 32-key chunk plus ~3 us for its
+// start, first and last steps and epilogue (per-tile timestamps: 0.77-0.83
+// us per chunk on long tiles, ~2.2 us of setup and epilogue; against 0.9 +
+// 2.0, trace step 20 191 -> 186 us, step 0 111 -> 110 us, the whole trace
+// within its noise).
 // The narrow streams (32-key chunks of 16 KiB of K and V) move ~5 GB/s per
 // wavefront until their sum nears the HBM rate they can reach, and bend
 // over smoothly there (timed per workgroup on trace steps: 1088 wavefronts
@@ -52,8 +56,8 @@ constexpr int kXcds = 8;                   // consecutive workgroups go to the X
 // and the outputs' writes no longer land under the streams (a sweep of
 // 5.7-8.5 TB/s over the 200-iteration trace: 7.0 the fastest, ~1% ahead of
 // 6.1, within the runs' noise elsewhere).
-constexpr double kWideChunkUs = 0.9;
-constexpr double kWideTileUs = 2.0;
+constexpr double kWideChunkUs = 0.8;
+constexpr double kWideTileUs = 3.0;
 constexpr double kNarrowWaveBytesPerUs = 5.0e3;
 constexpr double kNarrowHbmBytesPerUs = 7.0e6;
 constexpr double kChunkBytes = 16384.0;

@@ -107,7 +107,7 @@ def _check_wg_lists(plan, affine=True, slack=None):
     assert nwg % 8 == 0 and 0 < nwg <= 256 and len(off) == nwg + 1
     assert off[0] == 0 and off[-1] == nw and (np.diff(off) >= 0).all()
     assert (it[:nw, 5] == 0).all() and (it[:nw, 7] == -1).all()
-    cost = 0.9 * ((it[:nw, 6] + 31) // 32) + 2.0
+    cost = 0.8 * ((it[:nw, 6] + 31) // 32) + 3.0
     rows = nwg // 8
     nr = plan.narrow_rows
     share = 8.0 * (plan.wave_keys // 32) * 16384.0 / 30e3 if plan.num_waves else 0.0
